@@ -1,0 +1,185 @@
+"""fp64 CPU oracle for the FP8 variant: incoherent processing, per-block
+E4M3 quantisation, and a step-by-step simulation of FP8 attention.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module; the HIP path never does.
+
+Sources and readings:
+
+  * Incoherent processing x~ = H D x, with D a random +-1 diagonal and H a
+    Hadamard transform, applied to Q and K before quantisation: the
+    "FlashAttention-3" page (lyirs.cc), section "FP8 路径与低精度误差",
+    subsections "Incoherent processing 在做什么" and "为什么 Hadamard 适合放到内核里";
+    also the "FlashAttention-2/3" page, section "FlashAttention-3：拥抱 Hopper",
+    特性二 (a random orthogonal rotation).
+    Readings: H is the Sylvester-order Hadamard matrix,
+    H[i, j] = (-1)^popcount(i & j), normalised to be orthonormal (H / sqrt(d));
+    one D vector is shared by Q and K (needed for (HDq).(HDk) = q.k); V is
+    not rotated.
+  * Per-block quantisation with one scale per block: the "FlashAttention-2/3"
+    page, 特性三 (block-level online quantisation).  Readings: a block is
+    128 consecutive rows of one (b, h) over all d columns; the stored
+    dequantisation scale is s = amax / 448 (amax = 0 gives s = 1 and all
+    codes zero); code = E4M3 round-to-nearest-even of x * 448 / amax,
+    saturating at +-448.
+  * E4M3 itself: the FP8 formats named on the "FlashAttention-2/3" page
+    (特性二).  The codec below is the OCP "E4M3FN" encoding, written from
+    its definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits, subnormals m * 2^-9, no infinities, S.1111.111 is NaN, largest
+    finite value 448.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import attention as _attention_exact
+
+E4M3_MAX = 448.0
+E4M3_BIAS = 7
+
+
+def e4m3_decode(codes):
+    """Decode uint8 E4M3FN codes to fp64 (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sub = m.astype(np.float64) * 2.0 ** (1 - E4M3_BIAS - 3)          # m/8 * 2^-6
+    nrm = (1.0 + m / 8.0) * np.exp2((e - E4M3_BIAS).astype(np.float64))
+    val = np.where(e == 0, sub, nrm)
+    val = np.where((e == 0xF) & (m == 0x7), np.nan, val)
+    return sign * val
+
+
+# Non-negative finite values in code order (codes 0x00 .. 0x7E); the codes
+# are monotone in value, so a code's parity is its mantissa's parity.
+_POS_VALUES = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode(x):
+    """Round fp64 values to the nearest E4M3FN value, ties to the even code,
+    saturating at +-448.  NaN maps to 0x7F.  Negative values (including
+    those that round to zero, and -0.0) carry the sign bit."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_POS_VALUES, ax, side="left")      # first value >= ax
+    hi = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = ax - _POS_VALUES[lo]
+    d_hi = _POS_VALUES[hi] - ax
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(ax == _POS_VALUES[hi], hi, code)        # exact hits
+    code = code.astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def sylvester_hadamard(d):
+    """Dense unnormalised Sylvester Hadamard matrix, H_{2n} = [[H, H], [H, -H]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1), np.float64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def rotate(x, signs):
+    """Incoherent processing of the rows of x[..., d]: x~ = (H / sqrt(d)) D x.
+
+    Row vectors: x~ = (x * D) @ H^T / sqrt(d) (H is symmetric)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = sylvester_hadamard(d)
+    dx = x * np.asarray(signs, dtype=np.float64)
+    return (dx @ h.T) / np.sqrt(d)
+
+
+def block_quantize(x, block_rows=128):
+    """Per-(..., row block) E4M3 quantisation of x[..., N, d].
+
+    Returns (codes uint8 [..., N, d], scales fp64 [..., ceil(N/block_rows)],
+    y fp64 [..., N, d]) where y = x * 448 / amax is the value each code
+    rounds (kept so that tests can locate rounding boundaries)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-2]
+    nb = -(-n // block_rows)
+    lead = x.shape[:-2]
+    codes = np.empty(x.shape, np.uint8)
+    y = np.empty(x.shape, np.float64)
+    scales = np.empty(lead + (nb,), np.float64)
+    for b in range(nb):
+        r0, r1 = b * block_rows, min(n, (b + 1) * block_rows)
+        blk = x[..., r0:r1, :]
+        amax = np.max(np.abs(blk), axis=(-2, -1))
+        safe = np.where(amax > 0, amax, 1.0)
+        mult = np.where(amax > 0, E4M3_MAX / safe, 0.0)
+        yb = blk * mult[..., None, None]
+        y[..., r0:r1, :] = yb
+        codes[..., r0:r1, :] = e4m3_encode(yb)
+        scales[..., b] = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    return codes, scales, y
+
+
+def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False):
+    """The FP8 pre-pass: optional incoherent processing (signs given), then
+    per-block E4M3 quantisation.  Returns (codes, scales, y) with codes in
+    [..., N, d] or, if transpose_out, [..., d, N] order."""
+    xr = rotate(x, signs) if signs is not None else np.asarray(x, dtype=np.float64)
+    codes, scales, y = block_quantize(xr, block_rows)
+    if transpose_out:
+        codes = np.swapaxes(codes, -1, -2).copy()
+        y = np.swapaxes(y, -1, -2).copy()
+    return codes, scales, y
+
+
+def dequantize(codes, scales, block_rows=128, transposed=False):
+    """x^ = decode(code) * scale of its row block."""
+    c = np.swapaxes(codes, -1, -2) if transposed else codes
+    val = e4m3_decode(c)
+    n = val.shape[-2]
+    row_scale = np.repeat(scales, block_rows, axis=-1)[..., :n]
+    return val * row_scale[..., :, None]
+
+
+def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
+                            quantize_p=False, p_gain=256.0):
+    """Step-by-step simulation of FP8 attention (diagnostic floor).
+
+    1. Rotate Q and K with the shared signs (skipped if signs is None).
+    2. Block-quantise Q~, K~ and V and dequantise them.
+    3. Evaluate the exact definition on the dequantised values.  With
+       quantize_p, P is additionally rounded as E4M3(P * p_gain) / p_gain
+       before the product with V, while the row sums stay unquantised --
+       the kernel's own choice for its second product.
+    Returns fp64 (O, LSE).
+    """
+    qh = dequantize(*hadamard_rotate_quant(q, signs, block_rows)[:2], block_rows)
+    kh = dequantize(*hadamard_rotate_quant(k, signs, block_rows)[:2], block_rows)
+    vh = dequantize(*hadamard_rotate_quant(v, None, block_rows)[:2], block_rows)
+    if not quantize_p:
+        return _attention_exact(qh, kh, vh, scale, causal)
+    lead = qh.shape[:-2]
+    n, d = qh.shape[-2:]
+    qf, kf, vf = (a.reshape(-1, a.shape[-2], a.shape[-1]) for a in (qh, kh, vh))
+    o = np.empty((qf.shape[0], n, vf.shape[-1]))
+    lse = np.empty((qf.shape[0], n))
+    for h in range(qf.shape[0]):
+        s = (qf[h] @ kf[h].T) * scale
+        if causal:
+            s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+        m = s.max(1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(1)
+        eq = e4m3_decode(e4m3_encode(e * p_gain)) / p_gain
+        o[h] = (eq @ vf[h]) / l[:, None]
+        lse[h] = m + np.log(l)
+    return o.reshape(*lead, n, -1), lse.reshape(*lead, n)
+
+
+def rel_rms(a, b):
+    """||a - b||_F / ||b||_F."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.sqrt(np.sum((a - b) ** 2)) / np.sqrt(np.sum(b ** 2)))

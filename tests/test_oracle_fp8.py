@@ -1,0 +1,225 @@
+"""Pins for the FP8 side of the oracle: the E4M3 codec against the format's
+closed forms and torch's float8_e4m3fn, the Hadamard matrix against its
+closed form and a butterfly transform, the rotation's orthogonality, and the
+block quantiser and FP8 simulation on inputs where quantisation is lossless."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import (attention, block_quantize, dequantize, e4m3_decode, e4m3_encode,
+                    hadamard_rotate_quant, rotate, sylvester_hadamard)
+
+
+# ---------------------------------------------------------------- E4M3 codec
+# Closed-form values of the OCP E4M3FN encoding (1.4.3, bias 7).
+KNOWN = {
+    0x00: 0.0, 0x01: 2.0 ** -9, 0x02: 2.0 ** -8, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+    0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x3F: 1.875, 0x40: 2.0, 0x70: 128.0, 0x78: 256.0,
+    0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0,
+}
+
+
+def test_decode_known_values():
+    for code, val in KNOWN.items():
+        got = float(e4m3_decode(np.uint8(code)))
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(code)
+    assert np.isnan(e4m3_decode(np.uint8(0x7F))) and np.isnan(e4m3_decode(np.uint8(0xFF)))
+
+
+def test_decode_exhaustive_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert set(np.nonzero(nan)[0]) == {0x7F, 0xFF}
+    np.testing.assert_array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+
+
+def test_decode_is_monotone_and_bounded():
+    pos = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    assert pos.max() == 448.0
+
+
+def test_encode_round_trip_on_representable_values():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = e4m3_decode(codes)
+    np.testing.assert_array_equal(e4m3_encode(vals), codes)
+
+
+def test_encode_ties_to_even_and_saturation():
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02,
+             1.9375: 0x40, 15 * 2.0 ** -10: 0x08, 460.0: 0x7E, 1e6: 0x7E, -1e6: 0xFE,
+             -1.0625: 0xB8, 449.0: 0x7E, 432.0: 0x7E, 424.0: 0x7D}
+    for x, code in cases.items():
+        assert int(e4m3_encode(np.float64(x))) == code, x
+    assert int(e4m3_encode(np.float64(np.nan))) == 0x7F
+
+
+def test_encode_matches_torch_after_clamp():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1, 30, 300)])
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(e4m3_encode(x), ref)
+
+
+def test_encode_error_bound():
+    # Round to nearest: |x - decode(encode(x))| <= half the local spacing.
+    x = np.random.default_rng(1).uniform(-448, 448, 50000)
+    err = np.abs(e4m3_decode(e4m3_encode(x)) - x)
+    ax = np.abs(x)
+    spacing = np.where(ax < 2 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(ax, 2 ** -6))) - 3))
+    assert np.all(err <= spacing / 2 + 1e-12)
+
+
+# ---------------------------------------------------------------- Hadamard
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 128, 256])
+def test_hadamard_closed_form_and_orthogonality(d):
+    h = sylvester_hadamard(d)
+    i = np.arange(d)
+    pop = np.vectorize(lambda t: bin(t).count("1"))(i[:, None] & i[None, :])
+    np.testing.assert_array_equal(h, (-1.0) ** pop)
+    np.testing.assert_array_equal(h @ h.T, d * np.eye(d))
+
+
+def test_hadamard_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        sylvester_hadamard(96)
+
+
+def _fwht(x):
+    """In-place butterfly fast Walsh-Hadamard transform over the last axis."""
+    x = np.array(x, dtype=np.float64)
+    d = x.shape[-1]
+    hlen = 1
+    while hlen < d:
+        y = x.reshape(*x.shape[:-1], d // (2 * hlen), 2, hlen)
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a + b, a - b
+        x = y.reshape(*x.shape)
+        hlen *= 2
+    return x
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotation_equals_butterfly_fwht(d):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((5, 7, d))
+    signs = rng.integers(0, 2, d) * 2 - 1
+    np.testing.assert_allclose(rotate(x, signs), _fwht(x * signs) / math.sqrt(d), atol=1e-12)
+
+
+def test_rotation_preserves_inner_products_and_norms():
+    rng = np.random.default_rng(3)
+    d = 128
+    q, k = rng.standard_normal((40, d)), rng.standard_normal((30, d))
+    q[:, 5] *= 20
+    k[:, 5] *= 20
+    signs = rng.integers(0, 2, d) * 2 - 1
+    qr, kr = rotate(q, signs), rotate(k, signs)
+    np.testing.assert_allclose(qr @ kr.T, q @ k.T, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(np.linalg.norm(qr, axis=1), np.linalg.norm(q, axis=1), rtol=1e-14)
+    # different sign vectors for Q and K break the identity
+    other = -signs
+    other[0] = signs[0]
+    assert np.abs(rotate(q, signs) @ rotate(k, other).T - q @ k.T).max() > 1.0
+
+
+def test_rotation_spreads_an_outlier_channel():
+    d = 128
+    x = np.zeros((1, d))
+    x[0, 17] = 20.0
+    signs = np.ones(d)
+    xr = rotate(x, signs)
+    np.testing.assert_allclose(np.abs(xr), 20.0 / math.sqrt(d), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- block quantisation
+def test_block_scale_and_max_element():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2, 3, 300, 64))       # 300 rows: blocks of 128, 128, 44
+    codes, scales, y = block_quantize(x, 128)
+    assert scales.shape == (2, 3, 3)
+    for b, (r0, r1) in enumerate([(0, 128), (128, 256), (256, 300)]):
+        blk = x[:, :, r0:r1, :]
+        amax = np.abs(blk).max(axis=(-2, -1))
+        np.testing.assert_allclose(scales[..., b], amax / 448.0, rtol=1e-15)
+        cb = codes[:, :, r0:r1, :].reshape(2, 3, -1)
+        flat = blk.reshape(2, 3, -1)
+        idx = np.abs(flat).argmax(-1)
+        top = np.take_along_axis(cb, idx[..., None], -1)[..., 0]
+        sgn = np.take_along_axis(flat, idx[..., None], -1)[..., 0] < 0
+        np.testing.assert_array_equal(top, np.where(sgn, 0xFE, 0x7E))
+        assert np.all(np.abs(e4m3_decode(cb)) <= 448)
+
+
+def test_zero_block_gets_unit_scale():
+    x = np.zeros((1, 1, 256, 8))
+    x[0, 0, 200, 3] = -2.5
+    codes, scales, _ = block_quantize(x, 128)
+    assert scales[0, 0, 0] == 1.0 and np.all(e4m3_decode(codes[0, 0, :128]) == 0)
+    assert scales[0, 0, 1] == 2.5 / 448
+
+
+def _grid_exact(shape, seed, block_rows=128):
+    """Inputs that block quantisation represents exactly: E4M3 grid values
+    times a power-of-two block scale, with one +-448 per block."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x7F, shape).astype(np.uint8) | (rng.integers(0, 2, shape) << 7).astype(np.uint8)
+    vals = e4m3_decode(codes)
+    n = shape[-2]
+    for r0 in range(0, n, block_rows):
+        vals[..., r0, 0] = 448.0
+        vals[..., r0:r0 + block_rows, :] *= 2.0 ** rng.integers(-12, -4)
+    return vals
+
+
+def test_quantisation_is_lossless_on_grid_inputs():
+    x = _grid_exact((2, 2, 260, 32), 5)
+    for t in (False, True):
+        codes, scales, _ = hadamard_rotate_quant(x, None, 128, transpose_out=t)
+        if t:
+            assert codes.shape == (2, 2, 32, 260)
+        np.testing.assert_array_equal(dequantize(codes, scales, 128, transposed=t), x)
+
+
+def test_fp8_simulation_equals_exact_when_lossless():
+    """Rotated Q~, K~ and V on the E4M3 grid: the simulated FP8 attention then
+    equals the exact attention of the unrotated inputs (orthogonality)."""
+    B, H, N, d = 1, 2, 256, 64
+    rng = np.random.default_rng(6)
+    signs = rng.integers(0, 2, d) * 2 - 1
+    qt, kt, v = (_grid_exact((B, H, N, d), s) for s in (7, 8, 9))
+    h = sylvester_hadamard(d) / math.sqrt(d)
+    q = (qt @ h) * signs            # inverse of x~ = H D x  is  x = D H x~
+    k = (kt @ h) * signs
+    np.testing.assert_allclose(rotate(q, signs), qt, atol=1e-12)
+    scale = 1 / math.sqrt(d)
+    o_sim, lse_sim = oracle.attention_fp8_simulated(q, k, v, signs, scale)
+    o_ex, lse_ex = attention(q, k, v, scale)
+    np.testing.assert_allclose(o_sim, o_ex, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(lse_sim, lse_ex, rtol=0, atol=1e-9)
+
+
+def test_fp8_simulation_error_is_small_but_nonzero():
+    B, H, N, d = 1, 1, 256, 64
+    rng = np.random.default_rng(10)
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    signs = rng.integers(0, 2, d) * 2 - 1
+    o_ex, _ = attention(q, k, v, 0.125)
+    o_sim, _ = oracle.attention_fp8_simulated(q, k, v, signs, 0.125)
+    err = oracle.rel_rms(o_sim, o_ex)
+    # E4M3 keeps 3 mantissa bits: per-value relative error ~2-3 %.
+    assert 0.005 < err < 0.1
+    o_p, _ = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, quantize_p=True)
+    assert 0 < oracle.rel_rms(o_p, o_sim) < 0.06
+
+
+def test_rel_rms():
+    assert oracle.rel_rms([3.0, 4.0], [3.0, 4.0]) == 0.0
+    assert oracle.rel_rms([3.0, 4.0 + 5.0], [3.0, 4.0]) == pytest.approx(1.0)
