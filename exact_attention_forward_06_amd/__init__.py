@@ -1,0 +1,26 @@
+"""Exact-attention forward for AMD MI355X (gfx950).
+
+Public API (thin wrappers over the C ABI of libattn.so, include/attn.h):
+
+    attn_fwd(q, k, v, causal=False, softmax_scale=None) -> (o, lse)
+    hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False)
+        -> (codes, scales)
+    attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False)
+        -> (o, lse)
+    attn_fwd_fp8_e2e(q, k, v, signs, causal=False) -> (o, lse)
+"""
+from ._lib import AttnError, attn_fwd, attn_fwd_fp8, hadamard_rotate_quant, load
+
+
+def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=None):
+    """The whole FP8 path: rotate+quantise Q and K with the shared signs,
+    quantise V into the transposed layout, then the FP8 attention kernel."""
+    q8, sq = hadamard_rotate_quant(q, signs, stream=stream)
+    k8, sk = hadamard_rotate_quant(k, signs, stream=stream)
+    v8t, sv = hadamard_rotate_quant(v, None, transpose_out=True, stream=stream)
+    return attn_fwd_fp8(q8, sq, k8, sk, v8t, sv, causal=causal, softmax_scale=softmax_scale,
+                        stream=stream)
+
+
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "hadamard_rotate_quant",
+           "load"]

@@ -1,0 +1,158 @@
+"""ctypes binding of libattn.so: the same entry points as include/attn.h,
+taking torch device tensors.  Argument marshalling only -- every step of the
+computation runs in the HIP kernels; torch provides device memory and the
+current stream.  There is no fallback: if the library is missing or a call
+fails, an exception is raised."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "attn.h")
+
+ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+
+_c_i64_3 = ctypes.c_int64 * 3
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+_SIGNATURES = {
+    "attn_abi_version": ([], _i),
+    "attn_status_string": ([_i], ctypes.c_char_p),
+    "attn_last_error": ([], ctypes.c_char_p),
+    "attn_fwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i, _vp], _i),
+    "hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp], _i),
+    "attn_fwd_fp8": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, ctypes.c_float,
+                      _i, _vp], _i),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m exact_attention_forward_06_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = load()
+        raise AttnError(status, f"{lib.attn_status_string(status).decode()}: "
+                                f"{lib.attn_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _bhnd_strides(*ts):
+    s = ts[0].stride()
+    for t in ts:
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError("expected [B, H, N, d] tensors with a contiguous last dim")
+        if t.stride() != s or t.shape != ts[0].shape:
+            raise ValueError("q, k and v must share shape and strides")
+    return _c_i64_3(s[0], s[1], s[2])
+
+
+def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, return_lse=True,
+             stream=None):
+    """O, LSE = attention forward of device tensors q, k, v [B, H, N, d]
+    (fp32, fp16 or bf16).  Returns (o, lse) with lse fp32 [B, H, N]
+    (None when return_lse is False and no lse buffer is given)."""
+    lib = load()
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype among fp32, fp16, bf16")
+    B, H, N, d = q.shape
+    strides = _bhnd_strides(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides,
+                        _ptr(out), _ptr(lse), scale, int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, out=None,
+                          scales=None, stream=None):
+    """FP8 pre-pass of one [B, H, N, d] tensor: optional rotation by
+    (1/sqrt(d)) H diag(signs), per-block amax scale and E4M3 codes.
+    Returns (codes uint8 [B,H,N,d] or [B,H,d,N], scales fp32 [B,H,nblk])."""
+    lib = load()
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError("x must be fp32, fp16 or bf16")
+    B, H, N, d = x.shape
+    strides = _bhnd_strides(x)
+    nblk = -(-N // block_rows)
+    if out is None:
+        shape = (B, H, d, N) if transpose_out else (B, H, N, d)
+        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    if signs is not None and signs.dtype != torch.int8:
+        raise ValueError("signs must be int8")
+    _check(lib.hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides,
+                                     _ptr(signs), block_rows, int(bool(transpose_out)),
+                                     _ptr(out), _ptr(scales), _stream(stream)))
+    return out, scales
+
+
+def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False, softmax_scale=None,
+                 block_rows=128, out=None, lse=None, return_lse=True, stream=None):
+    """Attention forward on E4M3 codes (q8, k8 [B,H,N,d]; v8t [B,H,d,N]) with
+    per-block fp32 scales.  Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    lib = load()
+    B, H, N, d = q8.shape
+    for t in (q8, k8, v8t, q_scale, k_scale, v_scale):
+        if not t.is_contiguous():
+            raise ValueError("attn_fwd_fp8 takes contiguous tensors")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_fp8(B, H, N, d, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
+                            _ptr(v8t), _ptr(v_scale), block_rows, _ptr(out), _ptr(lse), scale,
+                            int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def declared_symbols(header: str = HEADER_PATH):
+    """Function names declared in include/attn.h."""
+    import re
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))

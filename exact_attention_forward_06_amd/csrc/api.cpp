@@ -1,0 +1,278 @@
+// C-ABI entry points of libattn: argument validation, dispatch, errors.
+// Every check runs before the first HIP call, so a rejected call has no side
+// effects; no C++ exception leaves this file.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) {
+  switch (dtype) {
+    case ATTN_F32: return 4;
+    case ATTN_F16: return 2;
+    case ATTN_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// Byte interval [lo, hi) touched by a strided [B, H, N, d] tensor.
+struct Span {
+  uintptr_t lo, hi;
+};
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Validates shape and strides of a [B, H, N, cols] tensor whose cols stride is
+// 1; fills `span`.  Returns ATTN_OK or an error status (message set).
+int check_strided(const char* name, const void* ptr, int B, int H, int N, int cols, int64_t sb,
+                  int64_t sh, int64_t sn, int esize, Span* span) {
+  if (ptr == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  if (sb < 0 || sh < 0 || sn < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "%s has a negative stride", name);
+  if (sn < cols && N > 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s rows overlap (n stride < d)", name);
+  if ((sb * esize) % 16 || (sh * esize) % 16 || (sn * esize) % 16)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "%s strides are not multiples of 16 bytes", name);
+  // extent in elements, computed in 128 bits to catch overflow
+  __int128 ext = (__int128)(B - 1) * sb + (__int128)(H - 1) * sh + (__int128)(N - 1) * sn + cols;
+  __int128 bytes = ext * esize;
+  if (bytes > ((__int128)1 << 62))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "%s extent overflows", name);
+  span->lo = reinterpret_cast<uintptr_t>(ptr);
+  span->hi = span->lo + (uintptr_t)bytes;
+  return ATTN_OK;
+}
+
+int check_dense(const char* name, const void* ptr, int64_t bytes, Span* span, bool align16 = true) {
+  if (ptr == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (align16 && !aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  if ((reinterpret_cast<uintptr_t>(ptr) & 3u) != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", name);
+  span->lo = reinterpret_cast<uintptr_t>(ptr);
+  span->hi = span->lo + (uintptr_t)bytes;
+  return ATTN_OK;
+}
+
+int check_sizes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  if ((int64_t)B * H * N > INT32_MAX)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "B*H*N exceeds 2^31-1");
+  if ((int64_t)B * H * N * d > ((int64_t)1 << 40))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "B*H*N*d exceeds 2^40 elements");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d is not one of 64, 128, 256", d);
+  return ATTN_OK;
+}
+
+int check_scale_causal(float softmax_scale, int causal) {
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  return ATTN_OK;
+}
+
+void strides_or_contiguous(const int64_t* s, int H, int N, int d, int64_t* sb, int64_t* sh,
+                           int64_t* sn) {
+  if (s) {
+    *sb = s[0];
+    *sh = s[1];
+    *sn = s[2];
+  } else {
+    *sn = d;
+    *sh = (int64_t)N * d;
+    *sb = (int64_t)H * N * d;
+  }
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_UNKNOWN_STATUS";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_fwd(int dtype, int B, int H, int N, int d, const void* q, const void* k, const void* v,
+             const int64_t* qkv_strides, void* o, float* lse, float softmax_scale, int causal,
+             void* stream) {
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (int st = check_scale_causal(softmax_scale, causal)) return st;
+  int64_t sb, sh, sn;
+  strides_or_contiguous(qkv_strides, H, N, d, &sb, &sh, &sn);
+  Span sq, sk, sv, so, sl{0, 0};
+  if (int st = check_strided("q", q, B, H, N, d, sb, sh, sn, es, &sq)) return st;
+  if (int st = check_strided("k", k, B, H, N, d, sb, sh, sn, es, &sk)) return st;
+  if (int st = check_strided("v", v, B, H, N, d, sb, sh, sn, es, &sv)) return st;
+  if (int st = check_dense("o", o, (int64_t)B * H * N * d * es, &so)) return st;
+  if (lse) {
+    if (int st = check_dense("lse", lse, (int64_t)B * H * N * 4, &sl, false)) return st;
+  }
+  if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "o overlaps an input");
+  if (lse && (overlaps(sl, sq) || overlaps(sl, sk) || overlaps(sl, sv) || overlaps(sl, so)))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "lse overlaps another tensor");
+
+  attn::FwdArgs a;
+  a.dtype = static_cast<attn::Dtype>(dtype);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.o = o;
+  a.lse = lse;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  bool supported = true;
+  hipError_t e = attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_fwd kernel for dtype %d d=%d", dtype, d);
+  return hip_status(e, "attn_fwd launch");
+}
+
+int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,
+                          const int64_t* x_strides, const int8_t* signs, int block_rows,
+                          int transpose_out, uint8_t* x8, float* scales, void* stream) {
+  const int es = elem_size(in_dtype);
+  if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", in_dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
+  if (transpose_out != 0 && transpose_out != 1)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "transpose_out must be 0 or 1");
+  if (transpose_out && N % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "transpose_out needs N a multiple of 16");
+  int64_t sb, sh, sn;
+  strides_or_contiguous(x_strides, H, N, d, &sb, &sh, &sn);
+  const int nblk = (N + block_rows - 1) / block_rows;
+  Span sx, s8, ss, sg{0, 0};
+  if (int st = check_strided("x", x, B, H, N, d, sb, sh, sn, es, &sx)) return st;
+  if (int st = check_dense("x8", x8, (int64_t)B * H * N * d, &s8)) return st;
+  if (int st = check_dense("scales", scales, (int64_t)B * H * nblk * 4, &ss, false)) return st;
+  if (signs) {
+    if (int st = check_dense("signs", signs, d, &sg, false)) return st;
+  }
+  if (overlaps(s8, sx) || overlaps(ss, sx) || overlaps(s8, ss) || (signs && (overlaps(sg, s8) || overlaps(sg, ss))))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs overlap inputs or each other");
+
+  attn::QuantArgs a;
+  a.dtype = static_cast<attn::Dtype>(in_dtype);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.x = x;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.signs = signs;
+  a.block_rows = block_rows;
+  a.transpose_out = transpose_out != 0;
+  a.x8 = x8;
+  a.scales = scales;
+  bool supported = true;
+  hipError_t e = attn::launch_hadamard_rotate_quant(a, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no hadamard_rotate_quant kernel for d=%d", d);
+  return hip_status(e, "hadamard_rotate_quant launch");
+}
+
+int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_scale,
+                 const uint8_t* k8, const float* k_scale, const uint8_t* v8t, const float* v_scale,
+                 int block_rows, void* o, float* lse, float softmax_scale, int causal,
+                 void* stream) {
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (int st = check_scale_causal(softmax_scale, causal)) return st;
+  if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
+  if (N % block_rows != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8 needs N a multiple of block_rows");
+  const int64_t codes = (int64_t)B * H * N * d;
+  const int64_t nsc = (int64_t)B * H * (N / block_rows) * 4;
+  Span a1, a2, a3, b1, b2, b3, so, sl{0, 0};
+  if (int st = check_dense("q8", q8, codes, &a1)) return st;
+  if (int st = check_dense("k8", k8, codes, &a2)) return st;
+  if (int st = check_dense("v8t", v8t, codes, &a3)) return st;
+  if (int st = check_dense("q_scale", q_scale, nsc, &b1, false)) return st;
+  if (int st = check_dense("k_scale", k_scale, nsc, &b2, false)) return st;
+  if (int st = check_dense("v_scale", v_scale, nsc, &b3, false)) return st;
+  if (int st = check_dense("o", o, codes * 2, &so)) return st;
+  if (lse) {
+    if (int st = check_dense("lse", lse, (int64_t)B * H * N * 4, &sl, false)) return st;
+  }
+  const Span ins[6] = {a1, a2, a3, b1, b2, b3};
+  for (const Span& s : ins) {
+    if (overlaps(so, s) || (lse && overlaps(sl, s)))
+      return fail(ATTN_ERR_INVALID_ARGUMENT, "an output overlaps an input");
+  }
+  if (lse && overlaps(sl, so)) return fail(ATTN_ERR_INVALID_ARGUMENT, "lse overlaps o");
+
+  attn::Fp8FwdArgs a;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.q8 = q8;
+  a.q_scale = q_scale;
+  a.k8 = k8;
+  a.k_scale = k_scale;
+  a.v8t = v8t;
+  a.v_scale = v_scale;
+  a.block_rows = block_rows;
+  a.o = o;
+  a.lse = lse;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  bool supported = true;
+  hipError_t e = attn::launch_attn_fwd_fp8(a, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_fwd_fp8 kernel for d=%d", d);
+  return hip_status(e, "attn_fwd_fp8 launch");
+}
+
+}  // extern "C"

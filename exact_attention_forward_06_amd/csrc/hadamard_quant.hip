@@ -1,0 +1,252 @@
+// FP8 pre-pass for gfx950: incoherent processing + per-block E4M3 codes.
+//
+// For each row x of one (b, h): x~ = H D x over the head dimension (D the
+// random +-1 diagonal, H the Sylvester Hadamard matrix), then per block of
+// 128 rows: amax = max |x~|, code = E4M3(x~ * 448 / amax), stored scale =
+// amax / (448 sqrt(d)).  The transform is left unnormalised in the kernel:
+// the codes do not depend on a common factor of the block, so the 1/sqrt(d)
+// of the orthonormal rotation only enters the stored scale.
+// Sources: the "FlashAttention-3" page, section "FP8 路径与低精度误差"
+// (x~ = H D x on Q and K; the Hadamard transform costs O(d log d) and is
+// bandwidth-bound) and the "FlashAttention-2/3" page, FlashAttention-3
+// 特性三 (one quantisation scale per block).
+//
+// gfx950 mapping (HBM-bound: one read of x, one byte written per element)
+//  * One workgroup (4 wave64) per (b, h, 128-row block); four lanes per row,
+//    each holding d/4 CONSECUTIVE elements loaded with 16-byte loads.  Of the
+//    log2(d) butterfly stages all but two are inside a lane; the last two
+//    (partners at lane distance 1 and 2) use DPP quad_perm swaps -- no LDS.
+//  * The whole block stays in registers until its amax is known (wave
+//    reduction through DPP, then 4 values through LDS), so HBM sees exactly
+//    one read and one write.
+//  * E4M3 codes come from v_cvt_pk_fp8_f32 (round to nearest even, OCP E4M3
+//    on gfx950) after clamping to +-448.
+//  * transpose_out writes [d][n] (the layout the FP8 attention kernel wants
+//    for V): codes are transposed through LDS so global stores stay 16-byte.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace attn {
+namespace {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int ROWS = 128;       // rows per scale block
+constexpr int NT = 256;         // threads per workgroup
+constexpr int LPR = 4;          // lanes per row
+constexpr int RPP = NT / LPR;   // rows per pass
+constexpr int PASSES = ROWS / RPP;
+
+struct QParams {
+  const char* x;
+  int64_t sb, sh, sn;
+  const int8_t* signs;
+  uint8_t* x8;
+  float* scales;
+  int H, N, nblk;
+  float scale_norm;   // 1/sqrt(d) for the rotated path, 1 otherwise
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<__bf16>(__bf16 v) { return (float)v; }
+template <>
+__device__ __forceinline__ float to_f32<_Float16>(_Float16 v) { return (float)v; }
+
+// value of lane ^ 1 / lane ^ 2 (DPP quad_perm [1,0,3,2] / [2,3,0,1])
+__device__ __forceinline__ float xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+template <typename T, int D, bool ROT, bool TRANS>
+__global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
+  constexpr int EPL = D / LPR;                  // elements per lane
+  constexpr int ES = sizeof(T);
+  constexpr int LOADS = EPL * ES / 16;          // 16-byte loads per lane per row
+  constexpr int PER16 = 16 / ES;                // elements per 16-byte load
+  static_assert(EPL * ES % 16 == 0, "lane slice must be whole 16-byte loads");
+
+  __shared__ float red[NT / 64];
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? D * ROWS : 16];
+
+  const int tid = threadIdx.x;
+  const int lr = tid & (LPR - 1);     // lane's quarter of the row
+  const int rr = tid / LPR;           // row within a pass
+  const int bh = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int r0 = blk * ROWS;
+  const char* xb = p.x + ((int64_t)b * p.sb + (int64_t)h * p.sh) * ES;
+
+  float v[PASSES][EPL];
+  float amax = 0.f;
+  float sg[ROT ? EPL : 1];
+  if constexpr (ROT) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) sg[i] = (float)p.signs[lr * EPL + i];
+  }
+
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = r0 + ps * RPP + rr;
+    const bool valid = row < p.N;
+    const char* src = xb + (int64_t)row * p.sn * ES + lr * EPL * ES;
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) {
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (valid) raw = *(const u32x4_t*)(src + l * 16);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int t = 0; t < PER16; ++t) v[ps][l * PER16 + t] = to_f32<T>(e[t]);
+    }
+    if constexpr (ROT) {
+      // D: sign flip
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[ps][i] *= sg[i];
+      // H: in-lane butterflies (partner distance 1 .. EPL/2)
+#pragma unroll
+      for (int hh = 1; hh < EPL; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if ((i & hh) == 0) {
+            const float a = v[ps][i], c = v[ps][i + hh];
+            v[ps][i] = a + c;
+            v[ps][i + hh] = a - c;
+          }
+      // cross-lane butterflies (partner distance EPL and 2*EPL elements)
+      const bool up1 = lr & 1, up2 = lr & 2;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const float o = xor1(v[ps][i]);
+        v[ps][i] = up1 ? o - v[ps][i] : v[ps][i] + o;
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const float o = xor2(v[ps][i]);
+        v[ps][i] = up2 ? o - v[ps][i] : v[ps][i] + o;
+      }
+    }
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(v[ps][i]));
+    }
+  }
+
+  // block amax
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float mult = amax > 0.f ? 448.f / amax : 0.f;
+  if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax > 0.f ? amax * p.scale_norm / 448.f : 1.f;
+
+  // codes
+  uint8_t* out = p.x8 + (int64_t)bh * p.N * D;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int lrow = ps * RPP + rr;
+    const int row = r0 + lrow;
+    unsigned words[EPL / 4];
+#pragma unroll
+    for (int w = 0; w < EPL / 4; ++w) {
+      float y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(v[ps][4 * w + t] * mult, -448.f), 448.f);
+      unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      words[w] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    }
+    if constexpr (!TRANS) {
+      if (row < p.N) {
+        uint8_t* dst = out + (int64_t)row * D + lr * EPL;
+#pragma unroll
+        for (int w = 0; w < EPL / 16; ++w) {
+          u32x4_t q = {words[4 * w], words[4 * w + 1], words[4 * w + 2], words[4 * w + 3]};
+          *(u32x4_t*)(dst + 16 * w) = q;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        tbuf[(lr * EPL + i) * ROWS + lrow] = (uint8_t)(words[i >> 2] >> (8 * (i & 3)));
+    }
+  }
+  if constexpr (TRANS) {
+    __syncthreads();
+    // out is [d][N] for this head: row = d index, 128 consecutive n per block
+    constexpr int CHUNKS = D * ROWS / 16;
+    const int nvalid = min(ROWS, p.N - r0);   // multiple of 16 (N % 16 == 0)
+#pragma unroll
+    for (int c = tid; c < CHUNKS; c += NT) {
+      const int dd = c / (ROWS / 16), cc = c % (ROWS / 16);
+      if (cc * 16 < nvalid)
+        *(u32x4_t*)(out + (int64_t)dd * p.N + r0 + cc * 16) = *(const u32x4_t*)(tbuf + dd * ROWS + cc * 16);
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_d(const QuantArgs& a, hipStream_t s) {
+  QParams p;
+  p.x = static_cast<const char*>(a.x);
+  p.sb = a.sb;
+  p.sh = a.sh;
+  p.sn = a.sn;
+  p.signs = a.signs;
+  p.x8 = a.x8;
+  p.scales = a.scales;
+  p.H = a.H;
+  p.N = a.N;
+  p.nblk = (a.N + ROWS - 1) / ROWS;
+  p.scale_norm = a.signs ? 1.f / sqrtf((float)D) : 1.f;
+  dim3 grid(p.nblk, a.B * a.H);
+  if (a.signs) {
+    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false>), grid, dim3(NT), 0, s, p);
+  } else {
+    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false>), grid, dim3(NT), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const QuantArgs& a, hipStream_t s, bool* ok) {
+  *ok = true;
+  switch (a.d) {
+    case 64: return launch_d<T, 64>(a, s);
+    case 128: return launch_d<T, 128>(a, s);
+    case 256: return launch_d<T, 256>(a, s);
+  }
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported) {
+  if (a.block_rows != ROWS) {
+    *supported = false;
+    return hipSuccess;
+  }
+  switch (a.dtype) {
+    case Dtype::BF16: return launch_t<__bf16>(a, stream, supported);
+    case Dtype::F16: return launch_t<_Float16>(a, stream, supported);
+    case Dtype::F32: return launch_t<float>(a, stream, supported);
+  }
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace attn

@@ -1,0 +1,57 @@
+// Private interface between the C-ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct FwdArgs {
+  Dtype dtype;
+  int B, H, N, d;
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t sb, sh, sn;   // element strides of q, k, v (b, h, n); d stride is 1
+  void* o;              // contiguous [B, H, N, d]
+  float* lse;           // [B, H, N] or nullptr
+  float scale;          // softmax scale (> 0)
+  bool causal;
+};
+
+struct QuantArgs {
+  Dtype dtype;
+  int B, H, N, d;
+  const void* x;
+  int64_t sb, sh, sn;
+  const int8_t* signs;  // nullptr = no rotation
+  int block_rows;
+  bool transpose_out;
+  uint8_t* x8;
+  float* scales;
+};
+
+struct Fp8FwdArgs {
+  int B, H, N, d;
+  const uint8_t* q8;
+  const float* q_scale;
+  const uint8_t* k8;
+  const float* k_scale;
+  const uint8_t* v8t;
+  const float* v_scale;
+  int block_rows;
+  void* o;              // bf16 [B, H, N, d]
+  float* lse;
+  float scale;
+  bool causal;
+};
+
+// Each returns hipSuccess or the launch error.  `supported` is set false
+// (and nothing launched) when no instantiation covers the request.
+hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream, bool* supported);
+hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported);
+hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* supported);
+
+}  // namespace attn

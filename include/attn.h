@@ -1,0 +1,159 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The library computes the fused exact-attention forward
+ *     O = softmax(Q K^T * softmax_scale) V        (per batch b, head h)
+ * with an online (running max / running sum) softmax tiled over row blocks of
+ * Q and an inner loop over blocks of K and V, so the N x N score matrix never
+ * reaches device memory; it also writes the per-row logsumexp (LSE).
+ * Sources: the attention definition is the displayed equation of the
+ * "FlashAttention-3" page (lyirs.cc), restated in its section
+ * "数学对象没变，执行图变了"; the tiled loop order (outer Q blocks, inner K/V
+ * blocks, running m_i and l_i, one normalisation at the end) is the
+ * "FlashAttention-2/3" page (compassingai.com), sections "在线 Softmax",
+ * "FlashAttention-2 的三大改进" and "技术原理"; the LSE output and the
+ * skipping of fully masked causal blocks are section 2.2 of the
+ * "Flash Attention V3" page (jsqmd.com).
+ *
+ * The FP8 variant follows the "FlashAttention-3" page, section
+ * "FP8 路径与低精度误差": incoherent processing x~ = H D x (random +-1 diagonal
+ * D, then a Hadamard transform over the head dimension) applied to Q and K,
+ * and per-block quantisation ("FlashAttention-2/3" page, FlashAttention-3
+ * 特性三).  It is two calls: hadamard_rotate_quant() per tensor, then
+ * attn_fwd_fp8().
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are device pointers (hipMalloc / torch device memory).  Q, K, V
+ *    are [B, H, N, d] with d contiguous; the b, h and n strides (in elements)
+ *    may be passed, NULL meaning contiguous.  Outputs are contiguous.
+ *  - N_q = N_k = N >= 1; d in {64, 128, 256}.  causal = 1 means query i sees
+ *    keys 0..i.
+ *  - The caller allocates and owns every buffer.  The library keeps no
+ *    pointer after a call returns, allocates no device memory and has no
+ *    global state; calls are thread-safe.  Outputs must not overlap inputs.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and is asynchronous: completion is observed by the caller.
+ *  - Arguments are validated before any HIP call, so a rejected call has no
+ *    side effects.  No C++ exception crosses this interface.
+ *  - Pointers must be 16-byte aligned and every row start (b, h, n strides
+ *    times the element size) must be a multiple of 16 bytes.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1, /* null pointer, size <= 0, overflow, bad stride,
+                                    misaligned pointer, overlapping output, bad flag */
+  ATTN_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement
+                                    (e.g. d not in {64,128,256}) */
+  ATTN_ERR_HIP = 3               /* a HIP runtime call failed; attn_last_error()
+                                    holds the runtime's message */
+};
+
+/* Element types of Q, K, V and O. */
+enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
+
+/* ABI version of the loaded library (ATTN_ABI_VERSION it was built with). */
+int attn_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(int status);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * attn_fwd -- exact attention forward in fp32, fp16 or bf16.
+ *
+ *   dtype          ATTN_F32, ATTN_F16 or ATTN_BF16: type of q, k, v and o.
+ *   B, H, N, d     batch, heads, sequence length, head dimension.
+ *   q, k, v        device [B, H, N, d] inputs (read only).
+ *   qkv_strides    host array of 3 int64 element strides (b, h, n) shared by
+ *                  q, k and v; the d stride is 1.  NULL = contiguous
+ *                  (H*N*d, N*d, d).
+ *   o              device output [B, H, N, d], contiguous, same dtype.
+ *   lse            device output [B, H, N] fp32, LSE_i = ln sum_j exp(s_ij)
+ *                  over the keys row i sees, s = softmax_scale * q.k;
+ *                  may be NULL (not written).
+ *   softmax_scale  positive, finite; callers pass 1/sqrt(d).
+ *   causal         0 or 1.
+ *   stream         hipStream_t or NULL.
+ *
+ * Accumulation is fp32 throughout; O is rounded to the output dtype once,
+ * after the final division by the row sum.
+ */
+int attn_fwd(int dtype, int B, int H, int N, int d,
+             const void* q, const void* k, const void* v,
+             const int64_t* qkv_strides,
+             void* o, float* lse,
+             float softmax_scale, int causal, void* stream);
+
+/*
+ * hadamard_rotate_quant -- FP8 pre-pass for one tensor.
+ *
+ * For every row x of x[B, H, N, d]: if `signs` is given, x~ = (1/sqrt(d)) H D x
+ * with D = diag(signs) and H the Sylvester-order Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)); otherwise x~ = x.  Then, per
+ * (b, h, block of block_rows consecutive rows) over all d columns:
+ * amax = max |x~|, scale = amax / 448 (1 if amax = 0), and
+ * code = E4M3FN round-to-nearest-even of x~ * 448 / amax (OCP FP8 E4M3,
+ * bias 7, max 448).  Dequantisation is x~ = decode(code) * scale.
+ *
+ *   in_dtype       ATTN_F32, ATTN_F16 or ATTN_BF16 (type of x).
+ *   B, H, N, d     shape of x; d in {64, 128, 256}.
+ *   x              device input; x_strides as qkv_strides of attn_fwd.
+ *   signs          device int8 [d] of +-1 (shared by the Q and K calls), or
+ *                  NULL for no rotation (V, and the unrotated comparison).
+ *   block_rows     rows per scale block; must be 128.
+ *   transpose_out  0: x8 is [B, H, N, d];  1: x8 is [B, H, d, N] (the layout
+ *                  attn_fwd_fp8 wants for V).
+ *   x8             device uint8 output codes.
+ *   scales         device fp32 output [B, H, ceil(N / block_rows)].
+ *   stream         hipStream_t or NULL.
+ */
+int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
+                          const void* x, const int64_t* x_strides,
+                          const int8_t* signs, int block_rows, int transpose_out,
+                          uint8_t* x8, float* scales, void* stream);
+
+/*
+ * attn_fwd_fp8 -- attention forward on FP8 E4M3 codes with per-block scales.
+ *
+ *   q8, k8         device uint8 [B, H, N, d] codes (hadamard_rotate_quant
+ *                  with the same signs for both), q_scale / k_scale device
+ *                  fp32 [B, H, N/block_rows].
+ *   v8t            device uint8 [B, H, d, N] codes (transpose_out = 1, no
+ *                  rotation), v_scale device fp32 [B, H, N/block_rows].
+ *   block_rows     128; N must be a multiple of block_rows.
+ *   o              device bf16 output [B, H, N, d].
+ *   lse            device fp32 [B, H, N] or NULL.
+ *   softmax_scale, causal, stream as in attn_fwd.
+ *
+ * Both products run on FP8 MFMA with fp32 accumulation: S = Q8 K8^T with
+ * the two block scales and softmax_scale folded into one factor per tile,
+ * and O += P V where P is rounded to E4M3 after multiplication by 2^8 (the
+ * row sums use the unrounded fp32 P).
+ */
+int attn_fwd_fp8(int B, int H, int N, int d,
+                 const uint8_t* q8, const float* q_scale,
+                 const uint8_t* k8, const float* k_scale,
+                 const uint8_t* v8t, const float* v_scale,
+                 int block_rows,
+                 void* o, float* lse,
+                 float softmax_scale, int causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

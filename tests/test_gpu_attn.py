@@ -1,0 +1,173 @@
+"""GPU parity of attn_fwd (fp32 / fp16 / bf16) against the fp64 oracle.
+
+Tolerances
+  bf16 / fp16 O: max |err| <= 2e-2 and mean |err| <= 2e-3 (fp32 accumulation);
+  fp32 O: max |err| <= 1e-4 (fp32 MFMA and exp2; errors ~1e-6 expected);
+  LSE (all dtypes): max |err| <= 1e-3 against the oracle's fp64 value.
+The oracle consumes the exact values the GPU receives (inputs upcast to fp64).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_forward_06_amd import attn_fwd
+from exact_attention_forward_06_amd.inputs import WORKLOADS, make_inputs, to_f64, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {  # dtype -> (max abs O, mean abs O, max abs LSE)
+    torch.bfloat16: (2e-2, 2e-3, 1e-3),
+    torch.float16: (2e-2, 2e-3, 1e-3),
+    torch.float32: (1e-4, 1e-5, 1e-4),
+}
+
+
+def _check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    tmax, tmean, tlse = TOL[dtype]
+    err = np.abs(o_gpu - o_ref)
+    lerr = np.abs(lse_gpu - lse_ref)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), what
+    assert err.max() <= tmax, f"{what}: max |O err| {err.max():.3e} > {tmax}"
+    assert err.mean() <= tmean, f"{what}: mean |O err| {err.mean():.3e} > {tmean}"
+    assert lerr.max() <= tlse, f"{what}: max |LSE err| {lerr.max():.3e} > {tlse}"
+    return err.max(), err.mean(), lerr.max()
+
+
+def _run(inp, causal, scale=None):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o, lse = attn_fwd(q, k, v, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _full_compare(inp, causal, dtype, what, scale=None):
+    d = inp["q"].shape[-1]
+    s = 1 / math.sqrt(d) if scale is None else scale
+    o, lse = _run(inp, causal, scale)
+    o_ref, lse_ref = oracle.attention(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), s, causal)
+    return _check(to_f64(o), lse.cpu().double().numpy(), o_ref, lse_ref, dtype, what)
+
+
+def _sample_rows(N, n_tiles_hint=128, seed=0, count=48):
+    rng = np.random.default_rng(seed)
+    edges = {0, 1, N - 1, N - 2}
+    for t in range(n_tiles_hint, N, n_tiles_hint * 7):
+        edges.update({t - 1, t})
+    rows = set(int(r) for r in rng.choice(N, count, replace=False)) | {e for e in edges if 0 <= e < N}
+    return np.array(sorted(rows))
+
+
+def _sampled_compare(inp, o, lse, causal, dtype, what, heads):
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, H, N, d = q.shape
+    s = 1 / math.sqrt(d)
+    og = []
+    orf = []
+    lg = []
+    lrf = []
+    for i, (b, h) in enumerate(heads):
+        rows = _sample_rows(N, seed=i)
+        o_r, l_r = oracle.attention_rows(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), rows, s, causal)
+        og.append(to_f64(o[b, h][rows]))
+        lg.append(lse[b, h][rows].double().cpu().numpy())
+        orf.append(o_r)
+        lrf.append(l_r)
+    return _check(np.concatenate(og), np.concatenate(lg), np.concatenate(orf), np.concatenate(lrf),
+                  dtype, what)
+
+
+# ---------------------------------------------------------------- the workloads
+def test_small_fp32_workload():
+    w = WORKLOADS["small_fp32"]
+    _full_compare(workload_inputs(w), w.causal, torch.float32, w.name)
+
+
+def test_bf16_n2048_workload_full():
+    w = WORKLOADS["bf16_n2048"]
+    _full_compare(workload_inputs(w), w.causal, torch.bfloat16, w.name)
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_8k", "bf16_d64", "bf16_d256"])
+def test_large_workload_sampled(name):
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    o, lse = _run(inp, w.causal)
+    o, lse = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(1)
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
+    _sampled_compare(inp, o, lse, w.causal, torch.bfloat16, name, heads)
+    # every row of every head: finite and LSE at least the largest single score term bound
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------- shapes and edges
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 77, 257, 300])
+def test_small_shapes(dtype, d, causal, N):
+    inp = make_inputs(1, 2, N, d, {torch.bfloat16: "bf16", torch.float16: "fp16",
+                                    torch.float32: "fp32"}[dtype], seed=100 + N + d)
+    _full_compare(inp, causal, dtype, f"{dtype} d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_tile_ragged(causal):
+    # several Q blocks and K/V tiles, ragged tail, B*H > 1
+    inp = make_inputs(2, 3, 1000, 128, "bf16", seed=7)
+    _full_compare(inp, causal, torch.bfloat16, f"N=1000 causal={causal}")
+
+
+def test_strided_bnhd_layout():
+    B, N, H, d = 2, 300, 4, 128
+    g = torch.Generator().manual_seed(3)
+    base = [torch.randn(B, N, H, d, generator=g).to(torch.bfloat16) for _ in range(3)]
+    dev = [t.cuda().permute(0, 2, 1, 3) for t in base]       # [B, H, N, d] views, n stride H*d
+    assert dev[0].stride() == (N * H * d, d, H * d, 1)
+    o, lse = attn_fwd(*dev, causal=True)
+    torch.cuda.synchronize()
+    ref = [to_f64(t.permute(0, 2, 1, 3)) for t in base]
+    o_ref, lse_ref = oracle.attention(*ref, 1 / math.sqrt(d), True)
+    _check(to_f64(o), lse.cpu().double().numpy(), o_ref, lse_ref, torch.bfloat16, "strided")
+
+
+def test_custom_scale_and_no_lse():
+    inp = make_inputs(1, 2, 200, 64, "bf16", seed=9)
+    _full_compare(inp, False, torch.bfloat16, "scale 0.3", scale=0.3)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o1, _ = attn_fwd(q, k, v, return_lse=False)
+    o2, _ = attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_bitwise_deterministic():
+    inp = make_inputs(2, 4, 1500, 128, "bf16", seed=11)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o1, l1 = attn_fwd(q, k, v, causal=True)
+    o2, l2 = attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_softmax_invariants_on_gpu():
+    # constant V rows -> O equals that row; zero Q -> O is the (prefix) mean of V
+    N, d = 333, 128
+    g = torch.Generator().manual_seed(5)
+    k = torch.randn(1, 1, N, d, generator=g).to(torch.bfloat16)
+    row = torch.randn(d, generator=g).to(torch.bfloat16)
+    v = row.expand(1, 1, N, d).contiguous()
+    q = torch.randn(1, 1, N, d, generator=g).to(torch.bfloat16)
+    o, _ = attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    assert np.abs(to_f64(o[0, 0]) - to_f64(row)[None, :]).max() <= 2e-2
+    qz = torch.zeros_like(q)
+    v2 = torch.randn(1, 1, N, d, generator=g).to(torch.bfloat16)
+    o, lse = attn_fwd(qz.cuda(), k.cuda(), v2.cuda(), causal=True)
+    torch.cuda.synchronize()
+    pref = np.cumsum(to_f64(v2[0, 0]), 0) / np.arange(1, N + 1)[:, None]
+    assert np.abs(to_f64(o[0, 0]) - pref).max() <= 2e-2
+    np.testing.assert_allclose(lse[0, 0].cpu().double().numpy(), np.log(np.arange(1, N + 1)), atol=1e-4)
