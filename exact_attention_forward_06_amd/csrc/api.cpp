@@ -154,6 +154,10 @@ int attn_fwd(int dtype, int B, int H, int N, int d, const void* q, const void* k
   }
   if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv))
     return fail(ATTN_ERR_INVALID_ARGUMENT, "o overlaps an input");
+  // the kernels address one head's K/V rows with 32-bit buffer offsets
+  // (including up to one tile of rows past N, which read as zero)
+  if (((int64_t)N + 256) * sn * es + (int64_t)d * es >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
   if (lse && (overlaps(sl, sq) || overlaps(sl, sk) || overlaps(sl, sv) || overlaps(sl, so)))
     return fail(ATTN_ERR_INVALID_ARGUMENT, "lse overlaps another tensor");
 

@@ -54,6 +54,7 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
 
 struct KParams {
   const char* q;
@@ -134,7 +135,8 @@ struct Traits<float> {
 };
 
 template <typename T, int D, int BN, int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 2)))
+void attn_fwd_kernel(KParams p) {
   using Tr = Traits<T>;
   using frag = typename Tr::frag;
   constexpr int ES = sizeof(T);
@@ -212,30 +214,32 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KParams p) {
   u32x4_t kreg[K_PER_T];
   u32x4_t vreg[V_PER_T][V_REGS];
 
+  // K/V rows come through raw buffer loads on a descriptor covering this
+  // head's rows 0..N-1: rows at or past N read as zero (the hardware range
+  // check), so ragged tiles need no branches and offsets stay 32-bit.
+  const int64_t head_extent = ((int64_t)(N - 1) * p.sn + D) * ES;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)head_extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)head_extent, 0x00020000);
+  const int rb = (int)row_bytes;
+
   auto load_tile = [&](int kt0) {
 #pragma unroll
     for (int t = 0; t < K_PER_T; ++t) {
       const int c = tid + t * NT;
       const int row = c / CH_ROW, col = c % CH_ROW;
-      const int key = kt0 + row;
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      kreg[t] = key < N ? *(const u32x4_t*)(kp + (int64_t)key * row_bytes + col * 16) : z;
+      kreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, (kt0 + row) * rb + col * 16, 0, 0));
     }
 #pragma unroll
     for (int t = 0; t < V_PER_T; ++t) {
       const int u = tid + t * NT;
-      u32x4_t z = {0u, 0u, 0u, 0u};
       if constexpr (VT) {
         const int kg = u / DCH, dc = u % DCH;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int key = kt0 + 4 * kg + kk;
-          vreg[t][kk] = key < N ? *(const u32x4_t*)(vp + (int64_t)key * row_bytes + dc * 16) : z;
-        }
+        for (int kk = 0; kk < 4; ++kk)
+          vreg[t][kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (kt0 + 4 * kg + kk) * rb + dc * 16, 0, 0));
       } else {
         const int row = u / CH_ROW, col = u % CH_ROW;
-        const int key = kt0 + row;
-        vreg[t][0] = key < N ? *(const u32x4_t*)(vp + (int64_t)key * row_bytes + col * 16) : z;
+        vreg[t][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (kt0 + row) * rb + col * 16, 0, 0));
       }
     }
   };
@@ -334,16 +338,28 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KParams p) {
           }
       }
 
-      // online softmax update (log2 domain)
+      // online softmax update (log2 domain).  The running max only moves
+      // when a row's tile max exceeds it by more than kTau: until then
+      // P = exp2(s c - m_run) <= 2^kTau, and the result is unchanged
+      // (O and l share the same reference), so the O rescale is skipped on
+      // almost every tile.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      const float m_tile = pair_max(mx) * c;
+      if (__any(m_tile > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -353,14 +369,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KParams p) {
           sacc[kb][i] = e;
           rs += e;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
+      l_run += rs;
 
       // O^T += V^T P^T
       if constexpr (KPACK == 8) {

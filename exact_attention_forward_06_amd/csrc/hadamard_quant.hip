@@ -20,7 +20,9 @@
 //    reduction through DPP, then 4 values through LDS), so HBM sees exactly
 //    one read and one write.
 //  * E4M3 codes come from v_cvt_pk_fp8_f32 (round to nearest even, OCP E4M3
-//    on gfx950) after clamping to +-448.
+//    on gfx950) after clamping to +-448; the value rounded is the quotient
+//    (x~ * 448) / amax with an FMA remainder correction, not x~ times a
+//    rounded 448 / amax, so exact rounding ties stay exact.
 //  * transpose_out writes [d][n] (the layout the FP8 attention kernel wants
 //    for V): codes are transposed through LDS so global stores stay 16-byte.
 #include "kernels.h"
@@ -149,7 +151,11 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float mult = amax > 0.f ? 448.f / amax : 0.f;
+  // y = (x~ * 448) / amax, formed as a product with 1/amax plus one FMA
+  // remainder correction: the remainder a - y0 * amax is exact in an FMA,
+  // so a quotient that is representable (e.g. an exact E4M3 rounding tie,
+  // frequent for 16-bit inputs whose x * 448 is exact) comes out exactly.
+  const float ramax = amax > 0.f ? 1.f / amax : 0.f;
   if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax > 0.f ? amax * p.scale_norm / 448.f : 1.f;
 
   // codes
@@ -163,7 +169,12 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
     for (int w = 0; w < EPL / 4; ++w) {
       float y[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(v[ps][4 * w + t] * mult, -448.f), 448.f);
+      for (int t = 0; t < 4; ++t) {
+        const float a = v[ps][4 * w + t] * 448.f;
+        const float y0 = a * ramax;
+        const float q = fmaf(fmaf(-y0, amax, a), ramax, y0);
+        y[t] = fminf(fmaxf(q, -448.f), 448.f);
+      }
       unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
       words[w] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
     }

@@ -114,8 +114,11 @@ def block_quantize(x, block_rows=128):
         blk = x[..., r0:r1, :]
         amax = np.max(np.abs(blk), axis=(-2, -1))
         safe = np.where(amax > 0, amax, 1.0)
-        mult = np.where(amax > 0, E4M3_MAX / safe, 0.0)
-        yb = blk * mult[..., None, None]
+        # the quotient (x * 448) / amax: x * 448 is exact in fp64 for every
+        # input of at most 50 significant bits and the division is correctly
+        # rounded, so a value that lies exactly on a rounding midpoint stays
+        # there and is decided by the ties-to-even rule
+        yb = np.where((amax > 0)[..., None, None], (blk * E4M3_MAX) / safe[..., None, None], 0.0)
         y[..., r0:r1, :] = yb
         codes[..., r0:r1, :] = e4m3_encode(yb)
         scales[..., b] = np.where(amax > 0, amax / E4M3_MAX, 1.0)

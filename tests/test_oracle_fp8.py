@@ -158,6 +158,27 @@ def test_block_scale_and_max_element():
         assert np.all(np.abs(e4m3_decode(cb)) <= 448)
 
 
+def test_exact_rounding_ties_resolve_to_even():
+    """Values lying exactly on an E4M3 rounding midpoint round to the even
+    code.  amax = 63/16: x = 153/16384 gives x * 448 / amax = 17/16 exactly
+    (between 1.0 = 0x38 and 1.125 = 0x39) and x = 225/8192 gives 25/8
+    (between 3.0 = 0x44 and 3.25 = 0x45).  amax = 3.125: x = 0.002288818359375
+    gives 0.328125 (between 0x2A and 0x2B); multiplying by a rounded 448/amax
+    instead would land just above that midpoint and give 0x2B."""
+    x = np.zeros((2, 1, 128, 8))
+    x[0, 0, 0, 0] = 63 / 16
+    x[0, 0, 1, 1] = 153 / 16384
+    x[0, 0, 2, 2] = -153 / 16384
+    x[0, 0, 3, 3] = 225 / 8192
+    x[1, 0, 0, 0] = 3.125
+    x[1, 0, 5, 5] = 0.002288818359375
+    codes, scales, y = block_quantize(x, 128)
+    assert y[0, 0, 1, 1] == 17 / 16 and y[0, 0, 3, 3] == 25 / 8 and y[1, 0, 5, 5] == 0.328125
+    assert codes[0, 0, 1, 1] == 0x38 and codes[0, 0, 2, 2] == 0xB8 and codes[0, 0, 3, 3] == 0x44
+    assert codes[1, 0, 5, 5] == 0x2A
+    assert codes[0, 0, 0, 0] == 0x7E and codes[1, 0, 0, 0] == 0x7E
+
+
 def test_zero_block_gets_unit_scale():
     x = np.zeros((1, 1, 256, 8))
     x[0, 0, 200, 3] = -2.5
