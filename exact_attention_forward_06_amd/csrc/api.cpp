@@ -1,7 +1,7 @@
 // C-ABI entry points of libattn: argument validation, dispatch, errors.
 // Every check runs before the first HIP call, so a rejected call has no side
 // effects; no C++ exception leaves this file.
-#include "../../include/attn.h"
+#include "attn.h"
 
 #include <hip/hip_runtime.h>
 
@@ -237,6 +237,8 @@ int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_s
   if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
   if (N % block_rows != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8 needs N a multiple of block_rows");
+  if ((int64_t)N * d >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one head's codes span 2 GiB or more");
   const int64_t codes = (int64_t)B * H * N * d;
   const int64_t nsc = (int64_t)B * H * (N / block_rows) * 4;
   Span a1, a2, a3, b1, b2, b3, so, sl{0, 0};

@@ -1,176 +1,177 @@
-// Exact-attention forward for gfx950: fp32 / fp16 / bf16 inputs, fp32
-// accumulation, causal or non-causal, per-row logsumexp output.
+// Exact-attention forward for gfx950, fp16 / bf16 inputs: fp32 accumulation,
+// causal or non-causal, per-row logsumexp output.  (fp32 inputs use
+// attn_fwd_f32.hip.)
 //
-// Method (see include/attn.h for the sources on the pages): the grid runs
-// over (batch, head, block of BLOCK_M query rows) -- the "outer loop over Q
+// Method (sources on the pages are listed in include/attn.h): the grid runs
+// over (batch, head, block of 128 query rows) -- the "outer loop over Q
 // blocks" of the FlashAttention-2 work partition ("FlashAttention-2/3" page,
 // FlashAttention-2 改进二) -- and each workgroup streams the K/V blocks of its
-// head through LDS, keeping the running row max m, running row sum l and the
-// unnormalised output in registers; O is divided by l once after the last
-// block (改进一) and LSE = m + ln l is stored.
+// head through LDS, keeping the running row max m, the running row sum l and
+// the unnormalised output in registers; O is divided by l once after the
+// last block (改进一) and LSE = m + ln l is stored.
 //
 // gfx950 mapping
-//  * One wave64 owns 32 query rows.  It computes S^T = K Q^T with 32x32 MFMAs
-//    (A = K rows from LDS, B = Q^T held in VGPRs for the whole loop), so the
-//    accumulator gives each lane ONE query (lane & 31) and 16 of the tile's
-//    keys; the other 16 keys of that query sit in lane ^ 32.  Row max / row
-//    sum are therefore in-lane reductions plus one v_permlane32_swap -- no
-//    LDS traffic, and each wave owns its rows outright (the page's
-//    "split Q across warps" partition, 改进三).
-//  * The key order inside a 32-key block is permuted (bits 2 and 3 of the
-//    A-operand row swapped) so that the S^T accumulator registers 8c..8c+7
-//    of a lane hold 8 CONSECUTIVE keys.  Rounded to 16 bits they are then
-//    directly the B operand (P^T) of O^T += V^T P^T -- P never leaves VGPRs.
-//  * V is stored transposed in LDS (Vt[d][key]) for the 16-bit types, so the
-//    A operand V^T reads 8 consecutive keys per lane (one ds_read_b128).
-//    The transpose is done in registers between the global load and the LDS
-//    store.  fp32 uses 32x32x2 MFMAs whose operands are single elements, so
-//    V stays in natural layout there.
-//  * K/V tiles are double-buffered in LDS: the global loads of tile j+1 are
-//    issued before the MFMAs of tile j and written to the other buffer after
-//    them, one barrier per tile.  Row pitches are padded by 16 bytes so the
-//    per-lane row reads of one MFMA operand fall in different banks.
-//  * Causal: K/V tiles wholly above the diagonal of the workgroup's rows are
-//    never loaded; a wave whose rows all precede a tile skips its math; the
-//    element mask is applied only where a tile straddles the diagonal or the
-//    ragged end of the sequence.
-//  * Workgroup ids are remapped so that consecutive Q blocks of a head land
-//    on the same XCD (hardware dispatch is round-robin over the 8 XCDs), and
-//    K/V of a head is re-read from that XCD's L2.  Under the causal mask the
-//    Q blocks with the most K/V tiles are issued first.
+//  * 4 wave64 per workgroup, 32 query rows per wave, two workgroups per CU
+//    (<= 256 VGPRs, 64 KiB LDS each) so every SIMD runs two independent waves:
+//    one wave's softmax VALU work issues while the other's MFMAs run.  (d=256
+//    needs more than 256 VGPRs and runs one wave per SIMD.)
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} with Q^T resident in
+//    VGPRs.  A lane's accumulator holds ONE query (lane & 31) and 16 of the
+//    tile's keys (the other 16 in lane ^ 32): row max / row sum are in-lane
+//    plus one v_permlane32_swap -- no LDS, each wave owns its rows (the
+//    page's "split Q across warps" partition, 改进三).
+//  * K rows are fed to that MFMA in a permuted order (bits 2 and 3 of the
+//    A-operand row swapped) so accumulator registers 8c..8c+7 hold 8
+//    consecutive keys; rounded to 16 bits they are directly the P^T operand
+//    of O^T += V^T P^T.  P never leaves VGPRs.
+//  * K and V tiles go global -> LDS with buffer_load_dwordx4 ... lds (no
+//    VGPR staging), double-buffered: the loads of tile j+1 are issued before
+//    the MFMAs of tile j.  Rows past N read as zero (buffer range check).
+//  * V stays in its natural [key][d] layout in LDS; the V^T operand is read
+//    with ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-d block
+//    and receives it transposed: one d per lane, 4 consecutive keys).
+//  * LDS rows are unpadded (the LDS-DMA writes 1 KiB per instruction
+//    contiguously), so 16-byte chunks are XOR-swizzled within a row; the
+//    swizzle makes both the K operand reads (16 rows, one chunk) and the
+//    transposed V reads (4 rows x 4 chunks) hit distinct banks.
+//  * Online softmax in the log2 domain with a lazy rescale: the running max
+//    only moves when a row's tile max exceeds it by more than 2^8, so
+//    P <= 256 and the O rescale is skipped on almost every tile.  Row sums
+//    are accumulated from the fp32 P (the LSE keeps fp32 accuracy).
+//  * Causal: K/V tiles wholly above the workgroup's diagonal are never
+//    loaded; a wave whose rows all precede a tile skips its math; the element
+//    mask runs only where a tile straddles the diagonal or the end of the
+//    sequence.
+//  * Workgroup ids are remapped so that the Q blocks of a head run on one
+//    XCD (the head's K/V is then re-read from that XCD's L2); under the
+//    causal mask the Q blocks with the most K/V tiles are issued first.
+#include "device_common.h"
 #include "kernels.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace attn {
+
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t s, bool* ok);
+
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
 
-struct KParams {
+// s_waitcnt vmcnt(0): this wave's global -> LDS copies have landed
+// (simm16 = vmcnt 0 | expcnt 7 << 4 | lgkmcnt 15 << 8).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+struct Params {
   const char* q;
   const char* k;
   const char* v;
   char* o;
   float* lse;
-  int64_t sb, sh, sn;   // element strides
+  int64_t sb, sh, sn;   // element strides of q, k, v
   int H, N, nmb, total;
   float scale_log2;     // softmax_scale * log2(e)
 };
 
-// Row of the S^T accumulator block -> key offset inside the 32-key block
-// (bits 2 and 3 swapped; an involution).
-__device__ __forceinline__ int swap_bits23(int r) {
-  return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-// Accumulator register i (0..15) of lane group g of a 32x32 MFMA holds row
-// (i/4)*8 + g*4 + i%4; after the permutation above that row is key
-// 16*(i/8) + 8*g + i%8 of the block.
-__device__ __forceinline__ int key_of_reg(int i, int g) { return 16 * (i >> 3) + 8 * g + (i & 7); }
-
-// Cross-half reductions: lanes l and l ^ 32 hold the two halves of a row.
-// v_permlane32_swap returns both register images; one of them carries the
-// partner lane's value and the other the lane's own, so a symmetric combine
-// of the pair is exact whichever image is which.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, x), false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
 template <typename T>
-struct Traits;
+struct Ops;
 
 template <>
-struct Traits<__bf16> {
-  static constexpr int KPACK = 8;     // elements per lane per MFMA operand
+struct Ops<__bf16> {
   using frag = bf16x8_t;
   static __device__ __forceinline__ f32x16_t mfma(frag a, frag b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ unsigned pack2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (unsigned)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+  static __device__ __forceinline__ unsigned pack2(float a, float b) {   // one v_cvt_pk_bf16_f32
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
   }
 };
 
 template <>
-struct Traits<_Float16> {
-  static constexpr int KPACK = 8;
+struct Ops<_Float16> {
   using frag = f16x8_t;
   static __device__ __forceinline__ f32x16_t mfma(frag a, frag b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ unsigned pack2(float a, float b) {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (unsigned)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+  static __device__ __forceinline__ unsigned pack2(float a, float b) {   // one v_cvt_pk_f16_f32
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2_t));
   }
 };
 
-template <>
-struct Traits<float> {
-  static constexpr int KPACK = 1;
-  using frag = float;
-  static __device__ __forceinline__ f32x16_t mfma(frag a, frag b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+// S^T accumulator row r of a 32-key block -> key (bits 2 and 3 swapped).
+__device__ __forceinline__ int key_of_row(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Register i (0..15) of lane group g holds key 16*(i/8) + 8*g + i%8 of the block.
+__device__ __forceinline__ int key_of_reg(int i, int g) { return 16 * (i >> 3) + 8 * g + (i & 7); }
+
+// XOR swizzle of the 16-byte chunks of an LDS row (depends on row & 15).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+
+// Issue one K tile and one V tile (TILE bytes each) global -> LDS into
+// `stage` (K at +0, V at +TILE).  DMA instruction t of a wave writes LDS bytes
+// [(t * NT + wave * 64) * 16, + 1024) of the tile, lane l's 16 bytes at
+// +16 l; off[t] is that lane's source offset relative to the tile's first row
+// and `base` (wave-uniform, the buffer's scalar offset) that row's offset.
+// (A free function: lambdas inside the kernel must not capture buffer
+// descriptors, or the host pass drops the kernel.)
+template <int LOADS, int NT, int TILE>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, char* stage,
+                                         int wave, int base, const int* off) {
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t) {
+    char* kdst = stage + (t * NT + wave * 64) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)kdst, 16, off[t], base, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(kdst + TILE), 16, off[t], base, 0, 0);
   }
-};
+}
 
-template <typename T, int D, int BN, int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 2)))
-void attn_fwd_kernel(KParams p) {
-  using Tr = Traits<T>;
-  using frag = typename Tr::frag;
-  constexpr int ES = sizeof(T);
-  constexpr int KPACK = Tr::KPACK;
-  constexpr int KSTEP = 2 * KPACK;          // MFMA K per instruction
-  constexpr int NKS = D / KSTEP;            // K-steps of S = K Q^T
-  constexpr int BLOCK_M = WAVES * 32;
-  constexpr int NT = WAVES * 64;
-  constexpr int NKB = BN / 32;              // 32-key blocks per tile
-  constexpr int NDB = D / 32;               // 32-wide d blocks of O^T
-  constexpr bool VT = (ES == 2);            // V transposed in LDS
-  constexpr int K_PITCH = D * ES + 16;
-  constexpr int V_PITCH = VT ? (BN * 2 + 16) : (D * ES + 16);
-  constexpr int V_ROWS = VT ? D : BN;
-  constexpr int K_BYTES = BN * K_PITCH;
-  constexpr int STAGE = K_BYTES + V_ROWS * V_PITCH;
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+template <typename T, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2)))
+void attn_fwd16_kernel(Params p) {
+  using Op = Ops<T>;
+  using frag = typename Op::frag;
+  constexpr int NT = 256, BLOCK_M = 128;
+  constexpr int RB = D * 2;                // LDS row bytes (K and V)
+  constexpr int TILE = BN * RB;            // bytes of one K (or V) tile
+  constexpr int STAGE = 2 * TILE;          // K tile then V tile
+  constexpr int NKS = D / 16;              // K-steps of S^T = K Q^T
+  constexpr int NKB = BN / 32;             // 32-key blocks per tile
+  constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
+  constexpr int NCC = BN / 16;             // 16-key chunks per tile (PV K-steps)
+  constexpr int LOADS = TILE / (NT * 16);  // LDS-DMA instructions per thread per tensor
+  static_assert(TILE % (NT * 16) == 0 && RB % 16 == 0, "tile split");
+  static_assert(2 * STAGE <= 65536, "LDS budget: two workgroups per CU");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // Two stages as two LDS objects: the compiler can then tell the in-flight
+  // global -> LDS copies into one stage from the reads of the other and does
+  // not make those reads wait for the copies.
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 31;     // query column of this lane / A-operand row
-  const int g = lane >> 5;     // lane group: k half of the operands
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int n = lane & 31;
+  const int g = lane >> 5;
   const int N = p.N;
 
-  // --- workgroup -> (b, h, Q block), XCD-aware
-  int logical;
-  {
-    const int w = blockIdx.x, tot = p.total;
-    const int qd = tot >> 3, rem = tot & 7, x = w & 7, s = w >> 3;
-    logical = x * qd + min(x, rem) + s;
-  }
+  const int logical = xcd_logical_id(blockIdx.x, p.total);
   const int bh = logical / p.nmb;
   int mb = logical - bh * p.nmb;
   if (CAUSAL) mb = p.nmb - 1 - mb;
@@ -178,266 +179,205 @@ void attn_fwd_kernel(KParams p) {
   const int h = bh - b * p.H;
   const int m0 = mb * BLOCK_M;
   const int wq0 = m0 + wave * 32;
-  const int64_t head_off = ((int64_t)b * p.sb + (int64_t)h * p.sh) * ES;
-  const char* qp = p.q + head_off;
-  const char* kp = p.k + head_off;
-  const char* vp = p.v + head_off;
-  const int64_t row_bytes = p.sn * ES;
+  const int q_row = wq0 + n;
+  const int64_t head_off = ((int64_t)b * p.sb + (int64_t)h * p.sh) * 2;
+  const int rbg = (int)(p.sn * 2);         // global row pitch in bytes
 
-  // --- Q^T fragments (B operand), resident for the whole loop
+  // Q^T fragments (B operand): lane (n, g) holds Q[q][16 ks + 8 g .. + 8]
   frag qf[NKS];
   {
-    const int qrow = wq0 + n;
-    const char* src = qp + (int64_t)qrow * row_bytes;
+    const char* src = p.q + head_off + (int64_t)q_row * rbg + g * 16;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const int col = ks * KSTEP + g * KPACK;
-      if constexpr (KPACK == 8) {
-        u32x4_t raw = {0u, 0u, 0u, 0u};
-        if (qrow < N) raw = *(const u32x4_t*)(src + col * ES);
-        qf[ks] = __builtin_bit_cast(frag, raw);
-      } else {
-        qf[ks] = (qrow < N) ? *(const float*)(src + col * ES) : 0.f;
-      }
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (q_row < N) raw = *(const u32x4_t*)(src + ks * 32);
+      qf[ks] = __builtin_bit_cast(frag, raw);
     }
   }
 
-  // --- K/V tile staging (global -> registers -> LDS)
-  constexpr int CH_ROW = D * ES / 16;              // 16-byte chunks per row
-  constexpr int K_PER_T = BN * CH_ROW / NT;
-  static_assert((BN * CH_ROW) % NT == 0, "K tile split");
-  constexpr int DCH = D / 8;                        // 8-element d chunks (16-bit V)
-  constexpr int V_PER_T = VT ? (BN / 4) * DCH / NT : K_PER_T;
-  static_assert(!VT || ((BN / 4) * DCH) % NT == 0, "V tile split");
-  constexpr int V_REGS = VT ? 4 : 1;
-
-  u32x4_t kreg[K_PER_T];
-  u32x4_t vreg[V_PER_T][V_REGS];
-
-  // K/V rows come through raw buffer loads on a descriptor covering this
-  // head's rows 0..N-1: rows at or past N read as zero (the hardware range
-  // check), so ragged tiles need no branches and offsets stay 32-bit.
-  const int64_t head_extent = ((int64_t)(N - 1) * p.sn + D) * ES;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)head_extent, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)head_extent, 0x00020000);
-  const int rb = (int)row_bytes;
-
-  auto load_tile = [&](int kt0) {
+  // K/V global -> LDS.  DMA instruction t of this wave writes LDS bytes
+  // [(t*NT + wave*64) * 16, +1024) of the tile; lane l's 16 bytes land at
+  // row P / RB, physical chunk (P % RB) / 16, which holds logical chunk
+  // physical ^ swz(row).
+  const int64_t extent = ((int64_t)(N - 1) * p.sn + D) * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), (short)0, (int)extent, 0x00020000);
+  int dma_off[LOADS];          // global byte offset of this lane's chunk, tile-relative
 #pragma unroll
-    for (int t = 0; t < K_PER_T; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / CH_ROW, col = c % CH_ROW;
-      kreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, (kt0 + row) * rb + col * 16, 0, 0));
-    }
-#pragma unroll
-    for (int t = 0; t < V_PER_T; ++t) {
-      const int u = tid + t * NT;
-      if constexpr (VT) {
-        const int kg = u / DCH, dc = u % DCH;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          vreg[t][kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (kt0 + 4 * kg + kk) * rb + dc * 16, 0, 0));
-      } else {
-        const int row = u / CH_ROW, col = u % CH_ROW;
-        vreg[t][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (kt0 + row) * rb + col * 16, 0, 0));
-      }
-    }
+  for (int t = 0; t < LOADS; ++t) {
+    const int pos = (t * NT + tid) * 16;
+    const int row = pos / RB;
+    const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
+    dma_off[t] = row * rbg + chunk * 16;
+  }
+  auto issue_tile = [&](int kt0, int stage) __attribute__((always_inline)) {
+    dma_tile<LOADS, NT, TILE>(krs, vrs, stage ? smem1 : smem0, wave, kt0 * rbg, dma_off);
   };
 
-  auto store_tile = [&](int stage) {
-    char* sK = smem + stage * STAGE;
-    char* sV = sK + K_BYTES;
-#pragma unroll
-    for (int t = 0; t < K_PER_T; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / CH_ROW, col = c % CH_ROW;
-      *(u32x4_t*)(sK + row * K_PITCH + col * 16) = kreg[t];
-    }
-#pragma unroll
-    for (int t = 0; t < V_PER_T; ++t) {
-      const int u = tid + t * NT;
-      if constexpr (VT) {
-        // 4 keys x 8 d  ->  8 rows of Vt, 4 keys (8 bytes) each
-        const int kg = u / DCH, dc = u % DCH;
-        const u32x4_t* r = vreg[t];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d0 = dc * 8 + 2 * e;
-          u32x2_t even, odd;
-          even[0] = (r[0][e] & 0xFFFFu) | (r[1][e] << 16);
-          even[1] = (r[2][e] & 0xFFFFu) | (r[3][e] << 16);
-          odd[0] = (r[0][e] >> 16) | (r[1][e] & 0xFFFF0000u);
-          odd[1] = (r[2][e] >> 16) | (r[3][e] & 0xFFFF0000u);
-          *(u32x2_t*)(sV + d0 * V_PITCH + kg * 8) = even;
-          *(u32x2_t*)(sV + (d0 + 1) * V_PITCH + kg * 8) = odd;
-        }
-      } else {
-        const int row = u / CH_ROW, col = u % CH_ROW;
-        *(u32x4_t*)(sV + row * V_PITCH + col * 16) = vreg[t][0];
-      }
-    }
-  };
+  // LDS read addresses (bytes from the start of a stage).
+  // K A-operand for (kb, ks): row kb*32 + key_of_row(n), logical chunk 2 ks + g.
+  const int krow = key_of_row(n);
+  const int kswz = swz<D>(krow);
+  // V^T A-operand (tr16): 16-lane group hq = lane / 16 covers d in
+  // [16 (hq & 1), +16) of a 32-wide d block and keys 8 (hq >> 1) + 4 half + e;
+  // lane j = 4 e + a of the group addresses d columns 4a .. 4a + 3.
+  const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
+  const int vg = hq >> 1;
+  const int vcol0 = (hq & 1) * 16 + 4 * ta;      // column inside the 32-wide d block
 
-  // --- running state
+  // Every K read is kaddr[ks] + kb*32*RB, every V^T read vaddr[db][half] +
+  // cc*16*RB (+ stage base): compile-time offsets on 16 per-lane addresses
+  // computed once here.
+  int kaddr[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) kaddr[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
+  int vaddr[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = vg * 8 + half * 4 + te;      // + cc*16 (does not change row & 15)
+      const int col = db * 32 + vcol0;
+      vaddr[db][half] = TILE + row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+    }
+
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s
+  float m_run = -INFINITY;   // running max of scale * log2(e) * s (possibly stale by < kTau)
   float l_run = 0.f;         // this lane's half of the running row sum
 
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const float c = p.scale_log2;
-  const int q_row = wq0 + n;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
-    const int kt0 = j * BN;
-    const bool more = (j + 1) < n_tiles;
-    if (more) load_tile(kt0 + BN);
-
-    const bool active = (wq0 < N) && (!CAUSAL || kt0 <= wq0 + 31);
-    if (active) {
-      const char* sK = smem + stage * STAGE;
-      const char* sV = sK + K_BYTES;
-
-      // S^T = K Q^T
-      f32x16_t sacc[NKB];
+  auto compute_tile = [&](int kt0, const char* sbase) __attribute__((always_inline)) {
+    // S^T = K Q^T
+    f32x16_t sacc[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const char* arow = sK + (kb * 32 + swap_bits23(n)) * K_PITCH + g * KPACK * ES;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          frag a;
-          if constexpr (KPACK == 8)
-            a = __builtin_bit_cast(frag, *(const u32x4_t*)(arow + ks * KSTEP * ES));
-          else
-            a = *(const float*)(arow + ks * KSTEP * ES);
-          sacc[kb] = Tr::mfma(a, qf[ks], sacc[kb]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(sbase + kb * 32 * RB + kaddr[ks]));
+        sacc[kb] = Op::mfma(a, qf[ks], sacc[kb]);
       }
+    }
 
-      // mask: ragged end of the sequence, and keys after the query (causal)
-      const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt0 + kb * 32 + key_of_reg(i, g);
-            const bool masked = (key >= N) || (CAUSAL && key > q_row);
-            if (masked) sacc[kb][i] = -INFINITY;
-          }
-      }
-
-      // online softmax update (log2 domain).  The running max only moves
-      // when a row's tile max exceeds it by more than kTau: until then
-      // P = exp2(s c - m_run) <= 2^kTau, and the result is unchanged
-      // (O and l share the same reference), so the O rescale is skipped on
-      // almost every tile.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      const float m_tile = pair_max(mx) * c;
-      if (__any(m_tile > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
+    // mask: end of the sequence, and keys after the query (causal)
+    const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_use));
-          sacc[kb][i] = e;
-          rs += e;
+          const int key = kt0 + kb * 32 + key_of_reg(i, g);
+          if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
         }
-      l_run += rs;
-
-      // O^T += V^T P^T
-      if constexpr (KPACK == 8) {
-        frag pf[BN / 16];
-#pragma unroll
-        for (int cc = 0; cc < BN / 16; ++cc) {
-          const int kb = cc >> 1, base = (cc & 1) * 8;
-          u32x4_t w;
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            w[t] = Tr::pack2(sacc[kb][base + 2 * t], sacc[kb][base + 2 * t + 1]);
-          pf[cc] = __builtin_bit_cast(frag, w);
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const char* arow = sV + (db * 32 + n) * V_PITCH + g * 16;
-#pragma unroll
-          for (int cc = 0; cc < BN / 16; ++cc) {
-            frag a = __builtin_bit_cast(frag, *(const u32x4_t*)(arow + cc * 32));
-            oacc[db] = Tr::mfma(a, pf[cc], oacc[db]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb * 32 + key_of_reg(i, g);
-              const float a = *(const float*)(sV + key * V_PITCH + (db * 32 + n) * 4);
-              oacc[db] = Tr::mfma(a, sacc[kb][i], oacc[db]);
-            }
-      }
     }
 
-    if (more) store_tile(stage ^ 1);
+    // online softmax (log2 domain, lazy rescale)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    const float m_tile = pair_max(mx) * c;
+    if (__any(m_tile > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    // P rounded to 16 bits as the P^T operand; row sums of the fp32 P
+    frag pf[NCC];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const int kb = cc >> 1, base = (cc & 1) * 8;
+      u32x4_t w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t], c, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t + 1], c, -m_use));
+        w[t] = Op::pack2(e0, e1);
+        rs0 += e0;
+        rs1 += e1;
+      }
+      pf[cc] = __builtin_bit_cast(frag, w);
+    }
+    l_run += rs0 + rs1;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sbase + cc * 16 * RB + vaddr[db][0]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sbase + cc * 16 * RB + vaddr[db][1]));
+        u32x4_t w;
+        w[0] = __builtin_bit_cast(u32x2_t, lo)[0];
+        w[1] = __builtin_bit_cast(u32x2_t, lo)[1];
+        w[2] = __builtin_bit_cast(u32x2_t, hi)[0];
+        w[3] = __builtin_bit_cast(u32x2_t, hi)[1];
+        oacc[db] = Op::mfma(__builtin_bit_cast(frag, w), pf[cc], oacc[db]);
+      }
+  };
+
+  // One K/V tile: issue the next tile's loads into the other stage, run this
+  // tile from `stage`, then wait for the loads and meet at the barrier.  The
+  // loop below calls it with literal stages 0 and 1, so after inlining every
+  // LDS address is a per-lane base plus an immediate.
+  auto step = [&](int j, int stage) __attribute__((always_inline)) {
+    const int kt0 = j * BN;
+    if (j + 1 < n_tiles) issue_tile(kt0 + BN, stage ^ 1);
+    const bool active = (wq0 < N) && (!CAUSAL || kt0 <= wq0 + 31);
+    if (active) compute_tile(kt0, stage ? smem1 : smem0);
+    wait_vmem();
     __syncthreads();
+  };
+
+  issue_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < n_tiles) step(j + 1, 1);
   }
 
-  // --- epilogue: O = O / l, LSE = m ln2 + ln l
+  // epilogue: O = O / l, LSE = m ln2 + ln l
   const float l_tot = pair_sum(l_run);
   if (q_row < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    char* orow = p.o + (((int64_t)bh * N + q_row) * D) * ES;
+    char* orow = p.o + (((int64_t)bh * N + q_row) * D) * 2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int d0 = db * 32 + t * 8 + g * 4;
-        const float v0 = oacc[db][4 * t + 0] * inv, v1 = oacc[db][4 * t + 1] * inv;
-        const float v2 = oacc[db][4 * t + 2] * inv, v3 = oacc[db][4 * t + 3] * inv;
-        if constexpr (ES == 2) {
-          u32x2_t w = {Tr::pack2(v0, v1), Tr::pack2(v2, v3)};
-          *(u32x2_t*)(orow + d0 * ES) = w;
-        } else {
-          f32x4_t w = {v0, v1, v2, v3};
-          *(f32x4_t*)(orow + d0 * ES) = w;
-        }
+        u32x2_t w = {Op::pack2(oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv),
+                     Op::pack2(oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv)};
+        *(u32x2_t*)(orow + d0 * 2) = w;
       }
     if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
   }
 }
 
-template <typename T, int D, int BN, int WAVES, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BLOCK_M = WAVES * 32;
-  KParams p;
+  constexpr int BLOCK_M = 128;
+  Params p;
   p.q = static_cast<const char*>(a.q);
   p.k = static_cast<const char*>(a.k);
   p.v = static_cast<const char*>(a.v);
@@ -451,31 +391,21 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   p.nmb = (a.N + BLOCK_M - 1) / BLOCK_M;
   p.total = a.B * a.H * p.nmb;
   p.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, WAVES, CAUSAL>), dim3(p.total), dim3(WAVES * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_fwd16_kernel<T, D, BN, CAUSAL>), dim3(p.total), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename T, int D, int BN, int WAVES>
-hipError_t launch_mask(const FwdArgs& a, hipStream_t s) {
-  return a.causal ? launch_one<T, D, BN, WAVES, true>(a, s) : launch_one<T, D, BN, WAVES, false>(a, s);
-}
-
 template <typename T>
-hipError_t launch_dtype(const FwdArgs& a, hipStream_t s, bool* ok) {
+hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool* ok) {
   *ok = true;
-  if constexpr (sizeof(T) == 2) {
-    switch (a.d) {
-      case 64: return launch_mask<T, 64, 128, 4>(a, s);
-      case 128: return launch_mask<T, 128, 64, 4>(a, s);
-      case 256: return launch_mask<T, 256, 32, 4>(a, s);
-    }
-  } else {
-    switch (a.d) {
-      case 64: return launch_mask<T, 64, 32, 4>(a, s);
-      case 128: return launch_mask<T, 128, 32, 4>(a, s);
-      case 256: return launch_mask<T, 256, 32, 4>(a, s);
-    }
+  auto go = [&](auto dc, auto bnc) -> hipError_t {
+    constexpr int D = decltype(dc)::value, BN = decltype(bnc)::value;
+    return a.causal ? launch_one<T, D, BN, true>(a, s) : launch_one<T, D, BN, false>(a, s);
+  };
+  switch (a.d) {
+    case 64: return go(std::integral_constant<int, 64>{}, std::integral_constant<int, 128>{});
+    case 128: return go(std::integral_constant<int, 128>{}, std::integral_constant<int, 64>{});
+    case 256: return go(std::integral_constant<int, 256>{}, std::integral_constant<int, 32>{});
   }
   *ok = false;
   return hipSuccess;
@@ -485,9 +415,9 @@ hipError_t launch_dtype(const FwdArgs& a, hipStream_t s, bool* ok) {
 
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream, bool* supported) {
   switch (a.dtype) {
-    case Dtype::BF16: return launch_dtype<__bf16>(a, stream, supported);
-    case Dtype::F16: return launch_dtype<_Float16>(a, stream, supported);
-    case Dtype::F32: return launch_dtype<float>(a, stream, supported);
+    case Dtype::BF16: return launch_t<__bf16>(a, stream, supported);
+    case Dtype::F16: return launch_t<_Float16>(a, stream, supported);
+    case Dtype::F32: return launch_attn_fwd_f32(a, stream, supported);
   }
   *supported = false;
   return hipSuccess;

@@ -6,28 +6,40 @@
 // Both products run on v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation,
 // as in the FP8 path of the "FlashAttention-3" page (section
 // "FP8 路径与低精度误差") with per-block quantisation ("FlashAttention-2/3"
-// page, FlashAttention-3 特性三); the online softmax is that of the bf16
-// kernel.
+// page, FlashAttention-3 特性三); the online softmax is that of the 16-bit
+// kernel (attn_fwd.hip), whose layout choices it shares.
 //
-//  * S: one 32x32x64 MFMA per 64 of d.  With 128-row blocks and 128-row
-//    workgroups, a K/V tile of 64 keys lies in one K block, so
-//    sQ * sK * softmax_scale * log2(e) is ONE scalar per tile.
-//  * P V: P is rounded to E4M3 after multiplication by 2^8 * sV_j / sVmax
+//  * S: one 32x32x64 MFMA per 64 of d.  128-row workgroups and 64-key tiles
+//    never straddle a 128-row scale block, so sQ * sK * softmax_scale *
+//    log2(e) is ONE scalar per tile.
+//  * Lazy rescale with threshold 2^4: P = exp2(s c - m_run) <= 16.
+//  * P V: P is rounded to E4M3 after multiplication by 16 * sV_j / sVmax
 //    (sV_j the tile's V block scale, sVmax the largest V block scale of the
-//    head): the factor enters the exp2 argument as a per-row bias, keeps
-//    P' <= 256 < 448 (no saturation) and lifts small P out of the subnormal
-//    range; the row sums are kept from the unrounded P.  At the end
-//    O = acc * sVmax / 256 / l.
+//    head); the factor enters the exp2 argument as a per-row bias, keeps
+//    P' <= 256 < 448 (no saturation) and keeps values down to 2^-10 of the
+//    row maximum out of the E4M3 subnormals; the row sums are kept from the
+//    unrounded P.  At the end O = acc * sVmax / 16 / l.
 //  * The S^T rows are permuted so that each lane group holds 16 CONSECUTIVE
 //    keys of a 32-key block; the 32 P^T bytes a lane feeds to one PV MFMA
-//    then pair with two 16-byte LDS reads of V8t per lane.
+//    then pair with two 16-byte LDS reads of V8t.
+//  * K8 and V8t tiles go global -> LDS with buffer_load_dwordx4 ... lds,
+//    double-buffered in two LDS objects, 16-byte chunks XOR-swizzled per row
+//    so the operand reads are bank-conflict free.
 #include "device_common.h"
 #include "kernels.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace attn {
 namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+constexpr float kTau8 = 4.f;         // lazy-rescale threshold (log2 units)
+constexpr float kPGain = 16.f;       // P' = P * kPGain * sV_j / sVmax <= 2^kTau8 * 16 = 256
 
 struct F8Params {
   const uint8_t* q8;
@@ -41,6 +53,8 @@ struct F8Params {
   int H, N, nmb, total, nblk;
   float scale_log2;
 };
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // S^T accumulator row r of a 32-key block -> key: lane group g = bit 2 of r
 // becomes bit 4 of the key, so group g holds keys 16g .. 16g+15.
@@ -58,26 +72,58 @@ __device__ __forceinline__ i32x8_t cat(u32x4_t lo, u32x4_t hi) {
   return r;
 }
 
-template <int D, int BN, int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_fp8_kernel(F8Params p) {
-  constexpr int BLOCK_M = WAVES * 32;
-  constexpr int NT = WAVES * 64;
+// XOR swizzles of the 16-byte chunks of an LDS row of RB bytes.  Sixteen
+// lanes read one chunk position from 16 rows at once; rows that share the
+// same 256 bytes of banks must map that chunk to different positions.
+// K rows are read in the key_of_row8 order ({0-7, 16-23} or {8-15, 24-31}
+// of a 32-key block), V8t rows consecutively.
+template <int RB>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (RB >= 256) return (row & 7) | (((row >> 4) & 1) << 3);
+  else if constexpr (RB == 128) return ((row >> 1) & 3) | (((row >> 4) & 1) << 2);
+  else return ((row >> 2) & 1) | (((row >> 4) & 1) << 1);   // RB == 64
+}
+template <int RB>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (RB >= 256) return row & 15;
+  else if constexpr (RB == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;                                 // RB == 64
+}
+
+// Global -> LDS copy of one tile of ROWS x RB bytes (row pitch `pitch` in
+// global memory) into `dst`; DMA instruction t of a wave writes LDS bytes
+// [(t * NT + wave * 64) * 16, + 1024), lane l at + 16 l.
+template <int LOADS, int NT>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, char* dst, int wave, int base, const int* off) {
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (t * NT + wave * 64) * 16), 16, off[t], base,
+                                             0, 0);
+}
+
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8_kernel(F8Params p) {
+  constexpr int NT = 256, BLOCK_M = 128;
   constexpr int NKS = D / 64;        // MFMA K-steps of S
   constexpr int NKB = BN / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // d blocks of O^T
   constexpr int NPV = BN / 64;       // PV MFMAs (64 keys each) per d block
-  constexpr int K_PITCH = D + 16;    // bytes
-  constexpr int V_PITCH = BN + 16;
-  constexpr int K_BYTES = BN * K_PITCH;
-  constexpr int STAGE = K_BYTES + D * V_PITCH;
-  static_assert(BLOCK_M == 128, "one Q scale block per workgroup");
+  constexpr int KRB = D;             // K8 tile row bytes (one key)
+  constexpr int VRB = BN;            // V8t tile row bytes (one d)
+  constexpr int K_BYTES = BN * KRB;
+  constexpr int STAGE = K_BYTES + D * VRB;
+  constexpr int KLOADS = K_BYTES / (NT * 16);
+  constexpr int VLOADS = D * VRB / (NT * 16);
+  static_assert(K_BYTES % (NT * 16) == 0 && (D * VRB) % (NT * 16) == 0, "tile split");
   static_assert(BN % 64 == 0 && 128 % BN == 0, "tile inside one K scale block");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int g = lane >> 5;
   const int N = p.N;
@@ -88,10 +134,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_fp8_kernel(F8Params p) {
   if (CAUSAL) mb = p.nmb - 1 - mb;
   const int m0 = mb * BLOCK_M;
   const int wq0 = m0 + wave * 32;
+  const int q_row = wq0 + n;
   const int64_t head = (int64_t)bh * N * D;
-  const uint8_t* qp = p.q8 + head;
-  const uint8_t* kp = p.k8 + head;
-  const uint8_t* vp = p.v8t + head;   // [D][N]
   const float* ksc = p.ks + (int64_t)bh * p.nblk;
   const float* vsc = p.vs + (int64_t)bh * p.nblk;
   const float sq = p.qs[(int64_t)bh * p.nblk + mb];
@@ -103,47 +147,49 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_fp8_kernel(F8Params p) {
   // Q8^T fragments: lane (n, g) holds Q8[q][64 ks + 32 g .. +32]
   i32x8_t qf[NKS];
   {
-    const uint8_t* src = qp + (int64_t)(wq0 + n) * D + g * 32;
+    const uint8_t* src = p.q8 + head + (int64_t)q_row * D + g * 32;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qf[ks] = cat(*(const u32x4_t*)(src + ks * 64), *(const u32x4_t*)(src + ks * 64 + 16));
   }
 
-  // staging: K tile BN x D bytes, V8t tile D x BN bytes
-  constexpr int KCH = BN * D / 16;
-  constexpr int VCH = D * BN / 16;
-  static_assert(KCH % NT == 0 && VCH % NT == 0, "tile split");
-  constexpr int K_PER_T = KCH / NT, V_PER_T = VCH / NT;
-  u32x4_t kreg[K_PER_T], vreg[V_PER_T];
+  // DMA source offsets (tile-relative) of this lane's chunks
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + head), (short)0, N * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v8t + head), (short)0, N * D, 0x00020000);
+  int koff[KLOADS], voff[VLOADS];
+#pragma unroll
+  for (int t = 0; t < KLOADS; ++t) {
+    const int pos = (t * NT + tid) * 16, row = pos / KRB;
+    koff[t] = row * D + (((pos % KRB) / 16) ^ swz_k<KRB>(row)) * 16;
+  }
+#pragma unroll
+  for (int t = 0; t < VLOADS; ++t) {
+    const int pos = (t * NT + tid) * 16, row = pos / VRB;
+    voff[t] = row * N + (((pos % VRB) / 16) ^ swz_v<VRB>(row)) * 16;
+  }
+  auto issue_tile = [&](int kt0, int stage) __attribute__((always_inline)) {
+    char* dst = stage ? smem1 : smem0;
+    dma<KLOADS, NT>(krs, dst, wave, kt0 * D, koff);
+    dma<VLOADS, NT>(vrs, dst + K_BYTES, wave, kt0, voff);
+  };
 
-  auto load_tile = [&](int kt0) {
+  // LDS read addresses: K A-operand rows kb*32 + key_of_row8(n), bytes
+  // 64 ks + 32 g (+16); V8t A-operand rows db*32 + n, keys 64 t + 16 g (+32).
+  const int krow = key_of_row8(n);
+  int kaddr[NKS][2];
 #pragma unroll
-    for (int t = 0; t < K_PER_T; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / (D / 16), col = c % (D / 16);
-      kreg[t] = *(const u32x4_t*)(kp + (int64_t)(kt0 + row) * D + col * 16);
-    }
+  for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-    for (int t = 0; t < V_PER_T; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / (BN / 16), col = c % (BN / 16);
-      vreg[t] = *(const u32x4_t*)(vp + (int64_t)row * N + kt0 + col * 16);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* sK = smem + stage * STAGE;
-    char* sV = sK + K_BYTES;
+    for (int hf = 0; hf < 2; ++hf)
+      kaddr[ks][hf] = krow * KRB + (((4 * ks + 2 * g + hf) ^ swz_k<KRB>(krow)) * 16);
+  int vaddr[NPV][2];
 #pragma unroll
-    for (int t = 0; t < K_PER_T; ++t) {
-      const int c = tid + t * NT;
-      *(u32x4_t*)(sK + (c / (D / 16)) * K_PITCH + (c % (D / 16)) * 16) = kreg[t];
-    }
+  for (int t = 0; t < NPV; ++t)
 #pragma unroll
-    for (int t = 0; t < V_PER_T; ++t) {
-      const int c = tid + t * NT;
-      *(u32x4_t*)(sV + (c / (BN / 16)) * V_PITCH + (c % (BN / 16)) * 16) = vreg[t];
-    }
-  };
+    for (int hf = 0; hf < 2; ++hf)
+      vaddr[t][hf] = K_BYTES + n * VRB + (((4 * t + 2 * hf + g) ^ swz_v<VRB>(n)) * 16);
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -155,121 +201,122 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_fp8_kernel(F8Params p) {
 
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
   const int n_tiles = kv_end / BN;     // N is a multiple of 128
-  const int q_row = wq0 + n;
   const float c0 = sq * p.scale_log2;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  auto compute_tile = [&](int kt0, const char* sb) __attribute__((always_inline)) {
+    const float c = c0 * ksc[kt0 >> 7];
+    const float fv = vsc[kt0 >> 7] * inv_svmax;     // in (0, 1]
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
-    const int kt0 = j * BN;
-    const bool more = (j + 1) < n_tiles;
-    if (more) load_tile(kt0 + BN);
-
-    const bool active = !CAUSAL || kt0 <= wq0 + 31;
-    if (active) {
-      const char* sK = smem + stage * STAGE;
-      const char* sV = sK + K_BYTES;
-      const float c = c0 * ksc[kt0 >> 7];
-      const float fv = vsc[kt0 >> 7] * inv_svmax;     // in (0, 1]
-
-      f32x16_t sacc[NKB];
+    f32x16_t sacc[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const char* arow = sK + (kb * 32 + key_of_row8(n)) * K_PITCH + g * 32;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const i32x8_t a = cat(*(const u32x4_t*)(arow + ks * 64), *(const u32x4_t*)(arow + ks * 64 + 16));
-          sacc[kb] = mfma_fp8(a, qf[ks], sacc[kb]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const i32x8_t a = cat(*(const lds_u32x4_t*)(sb + kb * 32 * KRB + kaddr[ks][0]),
+                              *(const lds_u32x4_t*)(sb + kb * 32 * KRB + kaddr[ks][1]));
+        sacc[kb] = mfma_fp8(a, qf[ks], sacc[kb]);
       }
+    }
 
-      if (CAUSAL && kt0 + BN - 1 > wq0) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt0 + kb * 32 + 16 * g + i;
-            if (key > q_row) sacc[kb][i] = -INFINITY;
-          }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      // e = P * 256 * fv  with P = exp2(s c - m)
-      const float bias = __builtin_amdgcn_logf(256.f * fv) - m_use;   // v_log_f32 is log2
-      float rs = 0.f;
+    if (CAUSAL && kt0 + BN - 1 > wq0) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, bias));
-          sacc[kb][i] = e;
-          rs += e;
+          const int key = kt0 + kb * 32 + 16 * g + i;
+          if (key > q_row) sacc[kb][i] = -INFINITY;
         }
-      l_run = l_run * alpha + rs * (1.f / (256.f * fv));
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-
-      // P^T operands: slot s of lane group g <-> key 64 t + 32 (s / 16) + 16 g + s % 16
-      i32x8_t pf[NPV];
-#pragma unroll
-      for (int t = 0; t < NPV; ++t)
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = 2 * t + (w >> 2);
-          const int i0 = (w & 3) * 4;
-          unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][i0], sacc[kb][i0 + 1], 0, false);
-          pf[t][w] = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][i0 + 2], sacc[kb][i0 + 3], lo, true);
-        }
-
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const char* arow = sV + (db * 32 + n) * V_PITCH + g * 16;
-#pragma unroll
-        for (int t = 0; t < NPV; ++t) {
-          const i32x8_t a = cat(*(const u32x4_t*)(arow + t * 64), *(const u32x4_t*)(arow + t * 64 + 32));
-          oacc[db] = mfma_fp8(a, pf[t], oacc[db]);
-        }
-      }
     }
 
-    if (more) store_tile(stage ^ 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    const float m_tile = pair_max(mx) * c;
+    if (__any(m_tile > m_run + kTau8)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // e = P * kPGain * fv  with P = exp2(s c - m_use)
+    const float lg = __builtin_amdgcn_logf(kPGain * fv);   // v_log_f32 is log2
+    const float bias = lg - m_use;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, bias));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, bias));
+        sacc[kb][i] = e0;
+        sacc[kb][i + 1] = e1;
+        rs0 += e0;
+        rs1 += e1;
+      }
+    l_run += (rs0 + rs1) * (1.f / (kPGain * fv));
+
+    // P^T operands: slot s of lane group g <-> key 64 t + 32 (s / 16) + 16 g + s % 16
+    i32x8_t pf[NPV];
+#pragma unroll
+    for (int t = 0; t < NPV; ++t)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = 2 * t + (w >> 2);
+        const int i0 = (w & 3) * 4;
+        unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][i0], sacc[kb][i0 + 1], 0, false);
+        pf[t][w] = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][i0 + 2], sacc[kb][i0 + 3], lo, true);
+      }
+
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < NPV; ++t) {
+        const i32x8_t a = cat(*(const lds_u32x4_t*)(sb + db * 32 * VRB + vaddr[t][0]),
+                              *(const lds_u32x4_t*)(sb + db * 32 * VRB + vaddr[t][1]));
+        oacc[db] = mfma_fp8(a, pf[t], oacc[db]);
+      }
+  };
+
+  auto step = [&](int j, int stage) __attribute__((always_inline)) {
+    const int kt0 = j * BN;
+    if (j + 1 < n_tiles) issue_tile(kt0 + BN, stage ^ 1);
+    const bool active = !CAUSAL || kt0 <= wq0 + 31;
+    if (active) compute_tile(kt0, stage ? smem1 : smem0);
+    wait_vmem();
     __syncthreads();
+  };
+
+  issue_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < n_tiles) step(j + 1, 1);
   }
 
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? svmax * (1.f / 256.f) / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? svmax * (1.f / kPGain) / l_tot : 0.f;
   __bf16* orow = p.o + ((int64_t)bh * N + q_row) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int d0 = db * 32 + t * 8 + g * 4;
-      u32x2_t w;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const __bf16 x = (__bf16)(oacc[db][4 * t + 2 * e] * inv);
-        const __bf16 y = (__bf16)(oacc[db][4 * t + 2 * e + 1] * inv);
-        w[e] = (unsigned)__builtin_bit_cast(unsigned short, x) |
-               ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
-      }
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const f32x2_t a = {oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv};
+      const f32x2_t b = {oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv};
+      u32x2_t w = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
+                   __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
       *(u32x2_t*)(orow + d0) = w;
     }
   if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
@@ -277,7 +324,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_fp8_kernel(F8Params p) {
 
 template <int D, int BN, bool CAUSAL>
 hipError_t launch_one(const Fp8FwdArgs& a, hipStream_t s) {
-  constexpr int WAVES = 4, BLOCK_M = 128;
+  constexpr int BLOCK_M = 128;
   F8Params p;
   p.q8 = a.q8;
   p.k8 = a.k8;
@@ -293,7 +340,7 @@ hipError_t launch_one(const Fp8FwdArgs& a, hipStream_t s) {
   p.total = a.B * a.H * p.nmb;
   p.nblk = a.N / a.block_rows;
   p.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, BN, WAVES, CAUSAL>), dim3(p.total), dim3(WAVES * 64), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, BN, CAUSAL>), dim3(p.total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -311,8 +358,8 @@ hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* su
     return hipSuccess;
   }
   switch (a.d) {
-    case 64: return launch_mask<64, 64>(a, stream);
-    case 128: return launch_mask<128, 64>(a, stream);
+    case 64: return launch_mask<64, 128>(a, stream);
+    case 128: return launch_mask<128, 128>(a, stream);
     case 256: return launch_mask<256, 64>(a, stream);
   }
   *supported = false;
