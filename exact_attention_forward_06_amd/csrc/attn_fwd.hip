@@ -123,46 +123,46 @@ __device__ __forceinline__ int swz(int row) {
   else return ((row & 3) << 2) | ((row >> 2) & 3);
 }
 
-// Issue one K tile and one V tile (TILE bytes each) global -> LDS into
-// `stage` (K at +0, V at +TILE).  DMA instruction t of a wave writes LDS bytes
-// [(t * NT + wave * 64) * 16, + 1024) of the tile, lane l's 16 bytes at
-// +16 l; off[t] is that lane's source offset relative to the tile's first row
-// and `base` (wave-uniform, the buffer's scalar offset) that row's offset.
-// (A free function: lambdas inside the kernel must not capture buffer
-// descriptors, or the host pass drops the kernel.)
-template <int LOADS, int NT, int TILE>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, char* stage,
-                                         int wave, int base, const int* off) {
+// Copy one tile (TILE = LOADS * NT * 16 bytes) global -> LDS at `dst`.  DMA
+// instruction t of a wave writes LDS bytes [(t * NT + wave * 64) * 16, + 1024),
+// lane l's 16 bytes at + 16 l; off[t] is that lane's source offset relative
+// to the tile's first row and `base` (wave-uniform, the buffer's scalar
+// offset) that row's offset.  (A free function: lambdas inside the kernel
+// must not capture buffer descriptors, or the host pass drops the kernel.)
+template <int LOADS, int NT>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int wave, int base, const int* off) {
 #pragma unroll
-  for (int t = 0; t < LOADS; ++t) {
-    char* kdst = stage + (t * NT + wave * 64) * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)kdst, 16, off[t], base, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(kdst + TILE), 16, off[t], base, 0, 0);
-  }
+  for (int t = 0; t < LOADS; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (t * NT + wave * 64) * 16), 16, off[t], base, 0, 0);
 }
 
 template <typename T, int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 2)))
 void attn_fwd16_kernel(Params p) {
   using Op = Ops<T>;
   using frag = typename Op::frag;
   constexpr int NT = 256, BLOCK_M = 128;
   constexpr int RB = D * 2;                // LDS row bytes (K and V)
   constexpr int TILE = BN * RB;            // bytes of one K (or V) tile
-  constexpr int STAGE = 2 * TILE;          // K tile then V tile
   constexpr int NKS = D / 16;              // K-steps of S^T = K Q^T
   constexpr int NKB = BN / 32;             // 32-key blocks per tile
   constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
   constexpr int NCC = BN / 16;             // 16-key chunks per tile (PV K-steps)
-  constexpr int LOADS = TILE / (NT * 16);  // LDS-DMA instructions per thread per tensor
+  constexpr int LOADS = TILE / (NT * 16);  // LDS-DMA instructions per thread per tile
   static_assert(TILE % (NT * 16) == 0 && RB % 16 == 0, "tile split");
-  static_assert(2 * STAGE <= 65536, "LDS budget: two workgroups per CU");
+  static_assert(4 * TILE <= 65536, "LDS budget: two workgroups per CU");
 
-  // Two stages as two LDS objects: the compiler can then tell the in-flight
-  // global -> LDS copies into one stage from the reads of the other and does
-  // not make those reads wait for the copies.
-  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
+  // Software pipeline over K/V tiles: iteration j issues the S MFMAs of tile
+  // j+1 next to the exp / pack VALU work of tile j, then the PV MFMAs of
+  // tile j next to the row max of tile j+1.  K therefore runs one tile ahead
+  // of V: iteration j reads K_{j+1} and V_j and copies K_{j+2}, V_{j+1} into
+  // the stages those two freed at the previous barrier.  Each stage is its
+  // own LDS object, so reads of one are never made to wait for the in-flight
+  // copies into another.
+  __shared__ __attribute__((aligned(1024))) char sk0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sk1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sv1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -212,24 +212,23 @@ void attn_fwd16_kernel(Params p) {
     const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
     dma_off[t] = row * rbg + chunk * 16;
   }
-  auto issue_tile = [&](int kt0, int stage) __attribute__((always_inline)) {
-    dma_tile<LOADS, NT, TILE>(krs, vrs, stage ? smem1 : smem0, wave, kt0 * rbg, dma_off);
+  auto copy_k = [&](int tile, int stage) __attribute__((always_inline)) {
+    dma_tile<LOADS, NT>(krs, stage ? sk1 : sk0, wave, tile * BN * rbg, dma_off);
+  };
+  auto copy_v = [&](int tile, int stage) __attribute__((always_inline)) {
+    dma_tile<LOADS, NT>(vrs, stage ? sv1 : sv0, wave, tile * BN * rbg, dma_off);
   };
 
-  // LDS read addresses (bytes from the start of a stage).
-  // K A-operand for (kb, ks): row kb*32 + key_of_row(n), logical chunk 2 ks + g.
+  // LDS read addresses.  K A-operand for (kb, ks): row kb*32 + key_of_row(n),
+  // logical chunk 2 ks + g.  V^T A-operand (tr16): 16-lane group hq covers d
+  // in [16 (hq & 1), +16) of a 32-wide d block and keys 8 (hq >> 1) + 4 half
+  // + e; lane j = 4 e + a of the group addresses d columns 4a .. 4a + 3.
+  // Every read is a per-lane address plus a compile-time offset.
   const int krow = key_of_row(n);
   const int kswz = swz<D>(krow);
-  // V^T A-operand (tr16): 16-lane group hq = lane / 16 covers d in
-  // [16 (hq & 1), +16) of a 32-wide d block and keys 8 (hq >> 1) + 4 half + e;
-  // lane j = 4 e + a of the group addresses d columns 4a .. 4a + 3.
   const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
   const int vg = hq >> 1;
-  const int vcol0 = (hq & 1) * 16 + 4 * ta;      // column inside the 32-wide d block
-
-  // Every K read is kaddr[ks] + kb*32*RB, every V^T read vaddr[db][half] +
-  // cc*16*RB (+ stage base): compile-time offsets on 16 per-lane addresses
-  // computed once here.
+  const int vcol0 = (hq & 1) * 16 + 4 * ta;
   int kaddr[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) kaddr[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
@@ -240,7 +239,7 @@ void attn_fwd16_kernel(Params p) {
     for (int half = 0; half < 2; ++half) {
       const int row = vg * 8 + half * 4 + te;      // + cc*16 (does not change row & 15)
       const int col = db * 32 + vcol0;
-      vaddr[db][half] = TILE + row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+      vaddr[db][half] = row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
     }
 
   f32x16_t oacc[NDB];
@@ -253,23 +252,26 @@ void attn_fwd16_kernel(Params p) {
 
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
+  // last tile this wave needs (causal: keys up to its last row)
+  const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
   const float c = p.scale_log2;
 
-  auto compute_tile = [&](int kt0, const char* sbase) __attribute__((always_inline)) {
-    // S^T = K Q^T
-    f32x16_t sacc[NKB];
+  // S^T = K Q^T of one tile from K stage `ks_lds`
+  auto qk = [&](f32x16_t (&sacc)[NKB], const char* ks_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(sbase + kb * 32 * RB + kaddr[ks]));
+        const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(ks_lds + kb * 32 * RB + kaddr[ks]));
         sacc[kb] = Op::mfma(a, qf[ks], sacc[kb]);
       }
     }
-
-    // mask: end of the sequence, and keys after the query (causal)
+  };
+  // mask keys past the end of the sequence / after the query, then the row
+  // max of the tile in log2 units
+  auto tile_max = [&](f32x16_t (&sacc)[NKB], int kt0) __attribute__((always_inline)) -> float {
     const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
@@ -280,14 +282,16 @@ void attn_fwd16_kernel(Params p) {
           if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
         }
     }
-
-    // online softmax (log2 domain, lazy rescale)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    const float m_tile = pair_max(mx) * c;
+    return pair_max(mx) * c;
+  };
+  // lazy rescale: move the running max only when the tile max exceeds it by
+  // more than kTau (then P = exp2(s c - m_run) <= 2^kTau)
+  auto update_max = [&](float m_tile) __attribute__((always_inline)) {
     if (__any(m_tile > m_run + kTau)) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
@@ -298,10 +302,10 @@ void attn_fwd16_kernel(Params p) {
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m_run = m_new;
     }
+  };
+  // P of one tile rounded to 16 bits (the P^T operand); row sums of the fp32 P
+  auto softmax_p = [&](f32x16_t (&sacc)[NKB], frag (&pf)[NCC]) __attribute__((always_inline)) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // P rounded to 16 bits as the P^T operand; row sums of the fp32 P
-    frag pf[NCC];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
@@ -318,14 +322,15 @@ void attn_fwd16_kernel(Params p) {
       pf[cc] = __builtin_bit_cast(frag, w);
     }
     l_run += rs0 + rs1;
-
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T from V stage `vs_lds`
+  auto pv = [&](const frag (&pf)[NCC], const char* vs_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) {
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sbase + cc * 16 * RB + vaddr[db][0]));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sbase + cc * 16 * RB + vaddr[db][1]));
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs_lds + cc * 16 * RB + vaddr[db][0]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs_lds + cc * 16 * RB + vaddr[db][1]));
         u32x4_t w;
         w[0] = __builtin_bit_cast(u32x2_t, lo)[0];
         w[1] = __builtin_bit_cast(u32x2_t, lo)[1];
@@ -335,25 +340,40 @@ void attn_fwd16_kernel(Params p) {
       }
   };
 
-  // One K/V tile: issue the next tile's loads into the other stage, run this
-  // tile from `stage`, then wait for the loads and meet at the barrier.  The
-  // loop below calls it with literal stages 0 and 1, so after inlining every
-  // LDS address is a per-lane base plus an immediate.
-  auto step = [&](int j, int stage) __attribute__((always_inline)) {
-    const int kt0 = j * BN;
-    if (j + 1 < n_tiles) issue_tile(kt0 + BN, stage ^ 1);
-    const bool active = (wq0 < N) && (!CAUSAL || kt0 <= wq0 + 31);
-    if (active) compute_tile(kt0, stage ? smem1 : smem0);
+  f32x16_t sA[NKB], sB[NKB];
+  frag pf[NCC];
+
+  // prologue: K_0, K_1, V_0 resident; S_0 and its max
+  copy_k(0, 0);
+  if (n_tiles > 1) copy_k(1, 1);
+  copy_v(0, 0);
+  wait_vmem();
+  __syncthreads();
+  if (w_tiles > 0) {
+    qk(sA, sk0);
+    update_max(tile_max(sA, 0));
+  }
+  __syncthreads();   // every wave is done with K stage 0 before K_2 lands there
+
+  // iteration j: S_j is in `cur`; K_{j+1} in K stage (j+1)&1, V_j in V stage j&1
+  auto step = [&](int j, int st, f32x16_t (&cur)[NKB], f32x16_t (&nxt)[NKB]) __attribute__((always_inline)) {
+    if (j + 2 < n_tiles) copy_k(j + 2, st);
+    if (j + 1 < n_tiles) copy_v(j + 1, st ^ 1);
+    if (j < w_tiles) {
+      // S_{j+1} MFMAs next to the exp / pack of P_j (S_{j+1} past the last
+      // tile reads a stale, in-bounds stage and is not used)
+      qk(nxt, st ? sk0 : sk1);
+      softmax_p(cur, pf);
+      // PV_j next to the row max of S_{j+1}
+      pv(pf, st ? sv1 : sv0);
+      if (j + 1 < w_tiles) update_max(tile_max(nxt, (j + 1) * BN));
+    }
     wait_vmem();
     __syncthreads();
   };
-
-  issue_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
   for (int j = 0; j < n_tiles; j += 2) {
-    step(j, 0);
-    if (j + 1 < n_tiles) step(j + 1, 1);
+    step(j, 0, sA, sB);
+    if (j + 1 < n_tiles) step(j + 1, 1, sB, sA);
   }
 
   // epilogue: O = O / l, LSE = m ln2 + ln l
