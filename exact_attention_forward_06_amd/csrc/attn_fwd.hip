@@ -1,6 +1,7 @@
-// Exact-attention forward for gfx950, fp16 / bf16 inputs: fp32 accumulation,
-// causal or non-causal, per-row logsumexp output.  (fp32 inputs use
-// attn_fwd_f32.hip.)
+// Exact-attention forward for gfx950, fp16 / bf16 inputs with d = 256: fp32
+// accumulation, causal or non-causal, per-row logsumexp output.  (d = 64 and
+// 128 run the 8-wave ping-pong kernel of attn_fwd_pp.hip, which shares this
+// file's operand layouts; fp32 inputs use attn_fwd_f32.hip.)
 //
 // Method (sources on the pages are listed in include/attn.h): the grid runs
 // over (batch, head, block of 128 query rows) -- the "outer loop over Q
@@ -45,7 +46,7 @@
 //  * Workgroup ids are remapped so that the Q blocks of a head run on one
 //    XCD (the head's K/V is then re-read from that XCD's L2); under the
 //    causal mask the Q blocks with the most K/V tiles are issued first.
-#include "device_common.h"
+#include "attn16_common.h"
 #include "kernels.h"
 
 #include <math.h>
@@ -55,86 +56,9 @@
 namespace attn {
 
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t s, bool* ok);
+hipError_t launch_attn_fwd16_pp(const FwdArgs& a, hipStream_t s, bool* ok);
 
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-
-constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
-
-// s_waitcnt vmcnt(0): this wave's global -> LDS copies have landed
-// (simm16 = vmcnt 0 | expcnt 7 << 4 | lgkmcnt 15 << 8).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-struct Params {
-  const char* q;
-  const char* k;
-  const char* v;
-  char* o;
-  float* lse;
-  int64_t sb, sh, sn;   // element strides of q, k, v
-  int H, N, nmb, total;
-  float scale_log2;     // softmax_scale * log2(e)
-};
-
-template <typename T>
-struct Ops;
-
-template <>
-struct Ops<__bf16> {
-  using frag = bf16x8_t;
-  static __device__ __forceinline__ f32x16_t mfma(frag a, frag b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack2(float a, float b) {   // one v_cvt_pk_bf16_f32
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
-  }
-};
-
-template <>
-struct Ops<_Float16> {
-  using frag = f16x8_t;
-  static __device__ __forceinline__ f32x16_t mfma(frag a, frag b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack2(float a, float b) {   // one v_cvt_pk_f16_f32
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2_t));
-  }
-};
-
-// S^T accumulator row r of a 32-key block -> key (bits 2 and 3 swapped).
-__device__ __forceinline__ int key_of_row(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Register i (0..15) of lane group g holds key 16*(i/8) + 8*g + i%8 of the block.
-__device__ __forceinline__ int key_of_reg(int i, int g) { return 16 * (i >> 3) + 8 * g + (i & 7); }
-
-// XOR swizzle of the 16-byte chunks of an LDS row (depends on row & 15).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  else return ((row & 3) << 2) | ((row >> 2) & 3);
-}
-
-// Copy one tile (TILE = LOADS * NT * 16 bytes) global -> LDS at `dst`.  DMA
-// instruction t of a wave writes LDS bytes [(t * NT + wave * 64) * 16, + 1024),
-// lane l's 16 bytes at + 16 l; off[t] is that lane's source offset relative
-// to the tile's first row and `base` (wave-uniform, the buffer's scalar
-// offset) that row's offset.  (A free function: lambdas inside the kernel
-// must not capture buffer descriptors, or the host pass drops the kernel.)
-template <int LOADS, int NT>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int wave, int base, const int* off) {
-#pragma unroll
-  for (int t = 0; t < LOADS; ++t)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (t * NT + wave * 64) * 16), 16, off[t], base, 0, 0);
-}
 
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 2)))
@@ -423,8 +347,6 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool* ok) {
     return a.causal ? launch_one<T, D, BN, true>(a, s) : launch_one<T, D, BN, false>(a, s);
   };
   switch (a.d) {
-    case 64: return go(std::integral_constant<int, 64>{}, std::integral_constant<int, 128>{});
-    case 128: return go(std::integral_constant<int, 128>{}, std::integral_constant<int, 64>{});
     case 256: return go(std::integral_constant<int, 256>{}, std::integral_constant<int, 32>{});
   }
   *ok = false;
@@ -434,6 +356,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool* ok) {
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream, bool* supported) {
+  // d = 64 and 128 in 16-bit types: the 8-wave ping-pong kernel (attn_fwd_pp.hip)
+  if ((a.dtype == Dtype::BF16 || a.dtype == Dtype::F16) && a.d <= 128) return launch_attn_fwd16_pp(a, stream, supported);
   switch (a.dtype) {
     case Dtype::BF16: return launch_t<__bf16>(a, stream, supported);
     case Dtype::F16: return launch_t<_Float16>(a, stream, supported);

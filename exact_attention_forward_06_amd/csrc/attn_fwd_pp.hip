@@ -1,0 +1,395 @@
+// Exact-attention forward for gfx950, fp16 / bf16 inputs, d = 64 and 128:
+// the "ping-pong" schedule.  Computes the same result as attn_fwd.hip (the
+// FlashAttention-2 forward of the "FlashAttention-2/3" page: outer loop over
+// Q blocks, online softmax, one division by l at the end, LSE = m + ln l),
+// with a different division of the work inside a compute unit.
+//
+//  * One workgroup of 8 wave64 per CU covers 256 query rows (32 per wave), so
+//    every K/V tile copied into LDS serves 8 waves.
+//  * Waves w and w + 4 run on the same SIMD.  Waves 0-3 (group 0) and 4-7
+//    (group 1) alternate between an MFMA phase -- S_j^T = K_j Q^T and
+//    O^T += V_{j-1}^T P_{j-1}^T -- and a softmax phase -- row max, lazy
+//    rescale and P_j = exp2(S_j c - m) -- one phase apart, with a workgroup
+//    barrier between phases.  Each SIMD thus always holds one wave issuing
+//    MFMAs and one issuing the VALU work of the softmax.  This is the
+//    producer / consumer overlap of softmax and matrix products that the
+//    "FlashAttention-3" page describes for Hopper warpgroups (section on
+//    warp specialisation and ping-pong scheduling), mapped onto two wave64
+//    per SIMD.
+//  * In the MFMA phase the K operand (ds_read_b128) and the V^T operand
+//    (ds_read_b64_tr_b16) are read a few MFMA pairs ahead of their use (the
+//    order is pinned with scheduling barriers); the S and O accumulator
+//    chains alternate so no MFMA waits on the previous one, and the wave
+//    raises its issue priority for the phase.
+//  * Each group's phase loop is compiled separately and every MFMA phase
+//    runs both products, so S and O stay in fixed registers: control flow
+//    that merged different phase variants made the compiler copy all of O
+//    at every phase.
+//  * K_j and V_{j-1} are copied global -> LDS (buffer_load ... lds) two
+//    phases before they are read, into one of two LDS stages; each stage is
+//    its own LDS object and the phase loop is unrolled so that every access
+//    names its stage at compile time.
+// Operand layouts, the key permutation, the LDS swizzle, the lazy rescale
+// and the causal skipping are those of attn_fwd.hip.
+#include "attn16_common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace attn {
+namespace {
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Workgroup barrier between phases.  s_barrier alone is not a memory
+// operation to the compiler, which could then move LDS reads of a stage
+// across it (ahead of the barrier that publishes the stage's copy); the
+// empty asm statements with a memory clobber pin every memory access to its
+// side of the barrier.  No wait is implied: copies are waited for with
+// wait_vmem() and each phase consumes its own LDS reads.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS writes have completed
+// (simm16 = vmcnt 63 | expcnt 7 << 4 | lgkmcnt 0 << 8).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <typename T, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_pp_kernel(Params p) {
+  using Op = Ops<T>;
+  using frag = typename Op::frag;
+  constexpr int NT = 512, BLOCK_M = 256;
+  constexpr int RB = D * 2;                // LDS row bytes (K and V)
+  constexpr int TILE = BN * RB;            // bytes of one K (or V) tile
+  constexpr int NKS = D / 16;              // K-steps of S^T = K Q^T
+  constexpr int NKB = BN / 32;             // 32-key blocks per tile
+  constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
+  constexpr int NCC = BN / 16;             // 16-key chunks per tile (PV K-steps)
+  constexpr int NOPS = NKB * NKS;          // MFMAs per tile of S^T, and of O^T
+  constexpr int LA = 3;                    // LDS read-ahead, in MFMA pairs
+  constexpr int LOADS = TILE / (NT * 16);  // LDS-DMA instructions per thread per tile
+  static_assert(NOPS == NDB * NCC, "S and O MFMA counts");
+  static_assert(TILE % (NT * 16) == 0 && RB % 16 == 0, "tile split");
+  static_assert(4 * TILE <= 160 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(1024))) char sk0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sk1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sv1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int group = wave >> 2;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int N = p.N;
+
+  const int logical = xcd_logical_id(blockIdx.x, p.total);
+  const int bh = logical / p.nmb;
+  int mb = logical - bh * p.nmb;
+  if (CAUSAL) mb = p.nmb - 1 - mb;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int m0 = mb * BLOCK_M;
+  const int wq0 = m0 + wave * 32;
+  const int q_row = wq0 + n;
+  const int64_t head_off = ((int64_t)b * p.sb + (int64_t)h * p.sh) * 2;
+  const int rbg = (int)(p.sn * 2);         // global row pitch in bytes
+
+  // Q^T fragments (B operand): lane (n, g) holds Q[q][16 ks + 8 g .. + 8]
+  frag qf[NKS];
+  {
+    const char* src = p.q + head_off + (int64_t)q_row * rbg + g * 16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (q_row < N) raw = *(const u32x4_t*)(src + ks * 32);
+      qf[ks] = __builtin_bit_cast(frag, raw);
+    }
+  }
+
+  // K/V global -> LDS: lane l of wave w, DMA instruction t, writes LDS bytes
+  // (t*NT + w*64 + l) * 16 of the stage = row P / RB, physical chunk
+  // (P % RB) / 16, which holds logical chunk physical ^ swz(row).
+  const int64_t extent = ((int64_t)(N - 1) * p.sn + D) * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), (short)0, (int)extent, 0x00020000);
+  int dma_off[LOADS];
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t) {
+    const int pos = (t * NT + tid) * 16;
+    const int row = pos / RB;
+    const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
+    dma_off[t] = row * rbg + chunk * 16;
+  }
+
+  // LDS read addresses (as in attn_fwd.hip): K A-operand row kb*32 +
+  // key_of_row(n), logical chunk 2 ks + g; V^T A-operand via tr16 reads.
+  const int krow = key_of_row(n);
+  const int kswz = swz<D>(krow);
+  const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
+  const int vg = hq >> 1;
+  const int vcol0 = (hq & 1) * 16 + 4 * ta;
+  int kaddr[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) kaddr[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
+  int vaddr[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = vg * 8 + half * 4 + te;
+      const int col = db * 32 + vcol0;
+      vaddr[db][half] = row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+    }
+
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY;   // running max of scale * log2(e) * s (possibly stale by < kTau)
+  float l_run = 0.f;         // this lane's half of the running row sum
+
+  const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  // tiles this wave needs (causal: keys up to its last row)
+  const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
+  const float c = p.scale_log2;
+
+  f32x16_t sacc[NKB];
+  frag pf[NCC];
+
+  auto tile_max = [&](int kt0) __attribute__((always_inline)) -> float {
+    const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 + kb * 32 + key_of_reg(i, g);
+          if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    return pair_max(mx) * c;
+  };
+  auto update_max = [&](float m_tile) __attribute__((always_inline)) {
+    if (__any(m_tile > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
+  };
+  auto softmax_p = [&]() __attribute__((always_inline)) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const int kb = cc >> 1, base = (cc & 1) * 8;
+      u32x4_t w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t], c, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t + 1], c, -m_use));
+        w[t] = Op::pack2(e0, e1);
+        rs0 += e0;
+        rs1 += e1;
+      }
+      pf[cc] = __builtin_bit_cast(frag, w);
+    }
+    l_run += rs0 + rs1;
+  };
+
+  // MFMA phase: S^T of tile j from K stage `kst` (DQ) and O^T += V^T P^T of
+  // tile j-1 from V stage `vst` (DP).  MFMA pair i is S block i % NKB, K-step
+  // i / NKB and O block i % NDB, key chunk i / NDB; its operands are read
+  // from LDS LA pairs earlier.
+  auto phase_mfma = [&](auto dq_c, auto dp_c, const char* kst, const char* vst) __attribute__((always_inline)) {
+    constexpr bool DQ = decltype(dq_c)::value != 0, DP = decltype(dp_c)::value != 0;
+    frag kf[NOPS], vf[NOPS];
+    auto load = [&](int i) __attribute__((always_inline)) {
+      if constexpr (DQ)
+        kf[i] = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(kst + (i % NKB) * 32 * RB + kaddr[i / NKB]));
+      if constexpr (DP) {
+        const char* vb = vst + (i / NDB) * 16 * RB;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vaddr[i % NDB][0]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vaddr[i % NDB][1]));
+        u32x4_t w;
+        w[0] = __builtin_bit_cast(u32x2_t, lo)[0];
+        w[1] = __builtin_bit_cast(u32x2_t, lo)[1];
+        w[2] = __builtin_bit_cast(u32x2_t, hi)[0];
+        w[3] = __builtin_bit_cast(u32x2_t, hi)[1];
+        vf[i] = __builtin_bit_cast(frag, w);
+      }
+    };
+    __builtin_amdgcn_s_setprio(1);   // MFMA issue first when both waves of the SIMD are ready
+    if constexpr (DQ) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < LA && i < NOPS; ++i) load(i);
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i) {
+      if (i + LA < NOPS) load(i + LA);
+      if constexpr (DQ) sacc[i % NKB] = Op::mfma(kf[i], qf[i / NKB], sacc[i % NKB]);
+      if constexpr (DP) oacc[i % NDB] = Op::mfma(vf[i], pf[i / NDB], oacc[i % NDB]);
+      // keep this order: the scheduler would otherwise pull each read down
+      // next to its MFMA and expose the LDS latency
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // pair j = K_j (j < n_tiles) and V_{j-1} (j >= 1), into stage ST
+  auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    if (j < n_tiles) dma_tile<LOADS, NT>(krs, ST ? sk1 : sk0, wave, j * BN * rbg, dma_off);
+    if (j >= 1) dma_tile<LOADS, NT>(vrs, ST ? sv1 : sv0, wave, (j - 1) * BN * rbg, dma_off);
+  };
+
+  // Phase t (t % 4 == TM) of group G.  Local phase u = t - G: even u = MFMA
+  // phase A_{u/2} (reads pair u/2), odd u = softmax phase B_{(u-1)/2}.  Pair
+  // j is read in phases 2j and 2j+1, copied during phase 2j-2 into stage
+  // j & 1 and waited for at the end of phase 2j-1.  The group is a template
+  // parameter so that each group's loop is straight-line code.
+  auto run = [&](auto g_c) __attribute__((always_inline)) {
+    constexpr int G = decltype(g_c)::value;
+    auto phase = [&](int t, auto tm_c) __attribute__((always_inline)) {
+      constexpr int TM = decltype(tm_c)::value;
+      if constexpr ((TM & 1) == 0) {
+        const int j = t / 2 + 1;
+        if (j <= n_tiles) copy_pair(j, ic<(TM == 0) ? 1 : 0>{});
+      }
+      const int u = t - G;
+      if (u >= 0 && u <= 2 * n_tiles) {
+        const int j = u >> 1;
+        if constexpr (((TM - G) & 1) == 0) {
+          constexpr int AST = TM >> 1;
+          const char* kst = AST ? sk1 : sk0;
+          const char* vst = AST ? sv1 : sv0;
+          // Both products run whenever either is needed: one code path keeps
+          // S and O in fixed registers (separate variants cost a copy of O
+          // per phase).  The unneeded one is harmless: S_j past the wave's
+          // last tile is never read, and in the first phase P is zero and V
+          // stage 0 is zero-filled, so O^T gains exactly zero.
+          if (j <= w_tiles) phase_mfma(ic<1>{}, ic<1>{}, kst, vst);
+        } else if (j < w_tiles) {
+          update_max(tile_max(j * BN));
+          softmax_p();
+        }
+      }
+      if constexpr ((TM & 1) == 1) wait_vmem();
+      if (t < 2 * n_tiles + 1) phase_barrier();
+    };
+    for (int t = 0; t < 2 * n_tiles + 2; t += 4) {
+      phase(t, ic<0>{});
+      phase(t + 1, ic<1>{});
+      if (t + 2 < 2 * n_tiles + 2) {
+        phase(t + 2, ic<2>{});
+        phase(t + 3, ic<3>{});
+      }
+    }
+  };
+
+  copy_pair(0, ic<0>{});
+#pragma unroll
+  for (int c = 0; c < TILE / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) pf[cc] = frag{};
+  wait_vmem();
+  wait_lds();
+  phase_barrier();
+  if (group == 0) run(ic<0>{});
+  else run(ic<1>{});
+
+  // epilogue: O = O / l, LSE = m ln2 + ln l
+  const float l_tot = pair_sum(l_run);
+  if (q_row < N) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    char* orow = p.o + (((int64_t)bh * N + q_row) * D) * 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int d0 = db * 32 + t * 8 + g * 4;
+        u32x2_t w = {Op::pack2(oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv),
+                     Op::pack2(oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv)};
+        *(u32x2_t*)(orow + d0 * 2) = w;
+      }
+    if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
+  }
+}
+
+template <typename T, int D, int BN, bool CAUSAL>
+hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BLOCK_M = 256;
+  Params p;
+  p.q = static_cast<const char*>(a.q);
+  p.k = static_cast<const char*>(a.k);
+  p.v = static_cast<const char*>(a.v);
+  p.o = static_cast<char*>(a.o);
+  p.lse = a.lse;
+  p.sb = a.sb;
+  p.sh = a.sh;
+  p.sn = a.sn;
+  p.H = a.H;
+  p.N = a.N;
+  p.nmb = (a.N + BLOCK_M - 1) / BLOCK_M;
+  p.total = a.B * a.H * p.nmb;
+  p.scale_log2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, BN, CAUSAL>), dim3(p.total), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool* ok) {
+  *ok = true;
+  auto go = [&](auto dc, auto bnc) -> hipError_t {
+    constexpr int D = decltype(dc)::value, BN = decltype(bnc)::value;
+    return a.causal ? launch_one<T, D, BN, true>(a, s) : launch_one<T, D, BN, false>(a, s);
+  };
+  switch (a.d) {
+    case 64: return go(ic<64>{}, ic<128>{});
+    case 128: return go(ic<128>{}, ic<64>{});
+  }
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+// d = 64 and 128 in bf16 / fp16; `supported` is false for anything else.
+hipError_t launch_attn_fwd16_pp(const FwdArgs& a, hipStream_t stream, bool* supported) {
+  switch (a.dtype) {
+    case Dtype::BF16: return launch_t<__bf16>(a, stream, supported);
+    case Dtype::F16: return launch_t<_Float16>(a, stream, supported);
+    default: break;
+  }
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace attn
