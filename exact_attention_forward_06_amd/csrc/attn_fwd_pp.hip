@@ -28,7 +28,10 @@
 //  * K_j and V_{j-1} are copied global -> LDS (buffer_load ... lds) two
 //    phases before they are read, into one of two LDS stages; each stage is
 //    its own LDS object and the phase loop is unrolled so that every access
-//    names its stage at compile time.
+//    names its stage at compile time.  Only group 1 issues the copies, at
+//    the start of its softmax phases: an LDS-DMA instruction holds the
+//    issuing wave while the CU's address unit takes its 1 KiB, which would
+//    stall the MFMA phase of the other group.
 // Operand layouts, the key permutation, the LDS swizzle, the lazy rescale
 // and the causal skipping are those of attn_fwd.hip.
 #include "attn16_common.h"
@@ -74,9 +77,10 @@ void attn_fwd_pp_kernel(Params p) {
   constexpr int NCC = BN / 16;             // 16-key chunks per tile (PV K-steps)
   constexpr int NOPS = NKB * NKS;          // MFMAs per tile of S^T, and of O^T
   constexpr int LA = 3;                    // LDS read-ahead, in MFMA pairs
-  constexpr int LOADS = TILE / (NT * 16);  // LDS-DMA instructions per thread per tile
+  constexpr int NTC = NT / 2;               // threads of the copying group (group 1)
+  constexpr int LOADS = TILE / (NTC * 16); // LDS-DMA instructions per copying thread per tile
   static_assert(NOPS == NDB * NCC, "S and O MFMA counts");
-  static_assert(TILE % (NT * 16) == 0 && RB % 16 == 0, "tile split");
+  static_assert(TILE % (NTC * 16) == 0 && RB % 16 == 0, "tile split");
   static_assert(4 * TILE <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) char sk0[TILE];
@@ -127,7 +131,7 @@ void attn_fwd_pp_kernel(Params p) {
   int dma_off[LOADS];
 #pragma unroll
   for (int t = 0; t < LOADS; ++t) {
-    const int pos = (t * NT + tid) * 16;
+    const int pos = (t * NTC + (tid & (NTC - 1))) * 16;
     const int row = pos / RB;
     const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
     dma_off[t] = row * rbg + chunk * 16;
@@ -266,8 +270,8 @@ void attn_fwd_pp_kernel(Params p) {
   // pair j = K_j (j < n_tiles) and V_{j-1} (j >= 1), into stage ST
   auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
-    if (j < n_tiles) dma_tile<LOADS, NT>(krs, ST ? sk1 : sk0, wave, j * BN * rbg, dma_off);
-    if (j >= 1) dma_tile<LOADS, NT>(vrs, ST ? sv1 : sv0, wave, (j - 1) * BN * rbg, dma_off);
+    if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, j * BN * rbg, dma_off);
+    if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j - 1) * BN * rbg, dma_off);
   };
 
   // Phase t (t % 4 == TM) of group G.  Local phase u = t - G: even u = MFMA
@@ -279,7 +283,7 @@ void attn_fwd_pp_kernel(Params p) {
     constexpr int G = decltype(g_c)::value;
     auto phase = [&](int t, auto tm_c) __attribute__((always_inline)) {
       constexpr int TM = decltype(tm_c)::value;
-      if constexpr ((TM & 1) == 0) {
+      if constexpr ((TM & 1) == 0 && G == 1) {
         const int j = t / 2 + 1;
         if (j <= n_tiles) copy_pair(j, ic<(TM == 0) ? 1 : 0>{});
       }
@@ -314,7 +318,7 @@ void attn_fwd_pp_kernel(Params p) {
     }
   };
 
-  copy_pair(0, ic<0>{});
+  if (group == 1) copy_pair(0, ic<0>{});
 #pragma unroll
   for (int c = 0; c < TILE / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll

@@ -141,8 +141,10 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  *
  * Both products run on FP8 MFMA with fp32 accumulation: S = Q8 K8^T with
  * the two block scales and softmax_scale folded into one factor per tile,
- * and O += P V where P is rounded to E4M3 after multiplication by 2^8 (the
- * row sums use the unrounded fp32 P).
+ * and O += P V where P is rounded to E4M3 after multiplication by a gain
+ * of 16 * sV_j / max_j sV_j (sV_j the scale of V's key block j), so that
+ * the V block scales fold into P and the lazy rescale threshold of 2^4
+ * keeps the scaled P at most 256; the row sums use the unrounded fp32 P.
  */
 int attn_fwd_fp8(int B, int H, int N, int d,
                  const uint8_t* q8, const float* q_scale,
