@@ -322,6 +322,316 @@ void attn_fwd_fp8_kernel(F8Params p) {
   if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant for d = 64 and 128 (the schedule of attn_fwd_pp.hip):
+// one workgroup of 8 wave64 covers 256 query rows; waves w and w + 4 share a
+// SIMD; waves 0-3 and 4-7 alternate, one phase apart, between an MFMA phase
+// (S_j^T = K8_j Q8^T and O^T += V8_{j-1}^T P8_{j-1}^T) and a softmax phase
+// (mask, scale, row max, lazy rescale, P' = exp2(s c + bias) rounded to
+// E4M3, row sums), with a workgroup barrier between phases.  Every wave's 32
+// rows lie inside one 128-row Q scale block; a 128-key tile is one K and one
+// V scale block.  K8 and V8t tiles are copied by waves 4-7 at the start of
+// their softmax phases, two phases ahead, into two stage objects each.
+
+__device__ __forceinline__ void phase_barrier8() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int V>
+using ic8 = std::integral_constant<int, V>;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8_pp_kernel(F8Params p) {
+  constexpr int BN = 128, NT = 512, NTC = 256, BLOCK_M = 256;
+  constexpr int NKS = D / 64;        // MFMA K-steps of S
+  constexpr int NKB = BN / 32;       // 32-key blocks per tile
+  constexpr int NDB = D / 32;        // d blocks of O^T
+  constexpr int NPV = BN / 64;       // PV MFMAs (64 keys each) per d block
+  constexpr int NOPS = NKB * NKS;    // MFMAs per tile of S^T, and of O^T
+  constexpr int LA = 2;              // LDS read-ahead, in MFMA pairs
+  constexpr int KRB = D;             // K8 tile row bytes (one key)
+  constexpr int VRB = BN;            // V8t tile row bytes (one d)
+  constexpr int K_BYTES = BN * KRB;
+  constexpr int V_BYTES = D * VRB;
+  constexpr int KLOADS = K_BYTES / (NTC * 16);
+  constexpr int VLOADS = V_BYTES / (NTC * 16);
+  static_assert(NOPS == NDB * NPV, "S and O MFMA counts");
+  static_assert(K_BYTES % (NTC * 16) == 0 && V_BYTES % (NTC * 16) == 0, "tile split");
+
+  __shared__ __attribute__((aligned(1024))) char sk0[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv0[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv1[V_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int N = p.N;
+
+  const int logical = xcd_logical_id(blockIdx.x, p.total);
+  const int bh = logical / p.nmb;
+  int mb = logical - bh * p.nmb;
+  if (CAUSAL) mb = p.nmb - 1 - mb;
+  const int m0 = mb * BLOCK_M;
+  const int wq0 = m0 + wave * 32;
+  const int q_row = wq0 + n;
+  const int64_t head = (int64_t)bh * N * D;
+  const float* ksc = p.ks + (int64_t)bh * p.nblk;
+  const float* vsc = p.vs + (int64_t)bh * p.nblk;
+  const float sq = (wq0 < N) ? p.qs[(int64_t)bh * p.nblk + (wq0 >> 7)] : 1.f;
+
+  float svmax = 0.f;
+  for (int i = 0; i < p.nblk; ++i) svmax = fmaxf(svmax, vsc[i]);
+  const float inv_svmax = 1.f / svmax;
+
+  // Q8^T fragments: lane (n, g) holds Q8[q][64 ks + 32 g .. +32]
+  i32x8_t qf[NKS];
+  {
+    const uint8_t* src = p.q8 + head + (int64_t)q_row * D + g * 32;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (q_row < N) {
+        lo = *(const u32x4_t*)(src + ks * 64);
+        hi = *(const u32x4_t*)(src + ks * 64 + 16);
+      }
+      qf[ks] = cat(lo, hi);
+    }
+  }
+
+  // copies by the 256 threads of group 1
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + head), (short)0, N * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v8t + head), (short)0, N * D, 0x00020000);
+  const int tg = tid & (NTC - 1);
+  int koff[KLOADS], voff[VLOADS];
+#pragma unroll
+  for (int t = 0; t < KLOADS; ++t) {
+    const int pos = (t * NTC + tg) * 16, row = pos / KRB;
+    koff[t] = row * D + (((pos % KRB) / 16) ^ swz_k<KRB>(row)) * 16;
+  }
+#pragma unroll
+  for (int t = 0; t < VLOADS; ++t) {
+    const int pos = (t * NTC + tg) * 16, row = pos / VRB;
+    voff[t] = row * N + (((pos % VRB) / 16) ^ swz_v<VRB>(row)) * 16;
+  }
+
+  const int krow = key_of_row8(n);
+  int kaddr[NKS][2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      kaddr[ks][hf] = krow * KRB + (((4 * ks + 2 * g + hf) ^ swz_k<KRB>(krow)) * 16);
+  int vaddr[NPV][2];
+#pragma unroll
+  for (int t = 0; t < NPV; ++t)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      vaddr[t][hf] = n * VRB + (((4 * t + 2 * hf + g) ^ swz_v<VRB>(n)) * 16);
+
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
+  const int n_tiles = kv_end / BN;     // N is a multiple of 128
+  const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
+  const float c0 = sq * p.scale_log2;
+
+  f32x16_t sacc[NKB];
+  i32x8_t pf[NPV];
+#pragma unroll
+  for (int t = 0; t < NPV; ++t)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) pf[t][w] = 0;
+
+  // MFMA phase: S^T of tile j and O^T += V^T P^T of tile j-1, operands read
+  // LA MFMA pairs ahead; pair i = S block i % NKB, K-step i / NKB and O block
+  // i % NDB, key half i / NDB.
+  auto phase_mfma = [&](const char* kst, const char* vst) __attribute__((always_inline)) {
+    i32x8_t kf[NOPS], vf[NOPS];
+    auto load = [&](int i) __attribute__((always_inline)) {
+      const char* kb_ = kst + (i % NKB) * 32 * KRB;
+      kf[i] = cat(*(const lds_u32x4_t*)(kb_ + kaddr[i / NKB][0]), *(const lds_u32x4_t*)(kb_ + kaddr[i / NKB][1]));
+      const char* vb_ = vst + (i % NDB) * 32 * VRB;
+      vf[i] = cat(*(const lds_u32x4_t*)(vb_ + vaddr[i / NDB][0]), *(const lds_u32x4_t*)(vb_ + vaddr[i / NDB][1]));
+    };
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < LA && i < NOPS; ++i) load(i);
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i) {
+      if (i + LA < NOPS) load(i + LA);
+      sacc[i % NKB] = mfma_fp8(kf[i], qf[i / NKB], sacc[i % NKB]);
+      oacc[i % NDB] = mfma_fp8(vf[i], pf[i / NDB], oacc[i % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // softmax phase of tile j (this wave needs it)
+  auto phase_softmax = [&](int j) __attribute__((always_inline)) {
+    const int kt0 = j * BN;
+    const float c = c0 * ksc[j];
+    const float fv = vsc[j] * inv_svmax;     // in (0, 1]
+    if (CAUSAL && kt0 + BN - 1 > wq0) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 + kb * 32 + 16 * g + i;
+          if (key > q_row) sacc[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    const float m_tile = pair_max(mx) * c;
+    if (__any(m_tile > m_run + kTau8)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    const float bias = __builtin_amdgcn_logf(kPGain * fv) - m_use;   // v_log_f32 is log2
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < NPV; ++t)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = 2 * t + (w >> 2);
+        const int i0 = (w & 3) * 4;
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0], c, bias));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0 + 1], c, bias));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0 + 2], c, bias));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0 + 3], c, bias));
+        const unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        pf[t][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, lo, true);
+        rs0 += e0 + e2;
+        rs1 += e1 + e3;
+      }
+    l_run += (rs0 + rs1) * (1.f / (kPGain * fv));
+  };
+
+  // pair j = K8 tile j (j < n_tiles) and V8t tile j-1 (j >= 1), into stage ST
+  auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    if (j < n_tiles) dma<KLOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, j * BN * D, koff);
+    if (j >= 1) dma<VLOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j - 1) * BN, voff);
+  };
+
+  // Phase t (t % 4 == TM) of group G: local phase u = t - G; even u = MFMA
+  // phase A_{u/2} reading pair u/2 from stage (u/2) & 1, odd u = softmax
+  // phase B_{(u-1)/2}.  Pair j is copied during phase 2j-2 (by group 1) and
+  // waited for at the end of phase 2j-1.
+  auto run = [&](auto g_c) __attribute__((always_inline)) {
+    constexpr int G = decltype(g_c)::value;
+    auto phase = [&](int t, auto tm_c) __attribute__((always_inline)) {
+      constexpr int TM = decltype(tm_c)::value;
+      if constexpr ((TM & 1) == 0 && G == 1) {
+        const int j = t / 2 + 1;
+        if (j <= n_tiles) copy_pair(j, ic8<(TM == 0) ? 1 : 0>{});
+      }
+      const int u = t - G;
+      if (u >= 0 && u <= 2 * n_tiles) {
+        const int j = u >> 1;
+        if constexpr (((TM - G) & 1) == 0) {
+          // both products run whenever either is needed (fixed registers for
+          // S and O); in the first phase P is zero and V stage 0 zero-filled
+          constexpr int AST = TM >> 1;
+          if (j <= w_tiles) phase_mfma(AST ? sk1 : sk0, AST ? sv1 : sv0);
+        } else if (j < w_tiles) {
+          phase_softmax(j);
+        }
+      }
+      if constexpr ((TM & 1) == 1) wait_vmem();
+      if (t < 2 * n_tiles + 1) phase_barrier8();
+    };
+    for (int t = 0; t < 2 * n_tiles + 2; t += 4) {
+      phase(t, ic8<0>{});
+      phase(t + 1, ic8<1>{});
+      if (t + 2 < 2 * n_tiles + 2) {
+        phase(t + 2, ic8<2>{});
+        phase(t + 3, ic8<3>{});
+      }
+    }
+  };
+
+  if (group == 1) copy_pair(0, ic8<0>{});
+#pragma unroll
+  for (int c = 0; c < V_BYTES / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
+  wait_vmem();
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zero-fill has landed
+  phase_barrier8();
+  if (group == 0) run(ic8<0>{});
+  else run(ic8<1>{});
+
+  const float l_tot = pair_sum(l_run);
+  if (q_row < N) {
+    const float inv = l_tot > 0.f ? svmax * (1.f / kPGain) / l_tot : 0.f;
+    __bf16* orow = p.o + ((int64_t)bh * N + q_row) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int d0 = db * 32 + t * 8 + g * 4;
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const f32x2_t a = {oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv};
+        const f32x2_t b = {oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv};
+        u32x2_t w = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
+                     __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
+        *(u32x2_t*)(orow + d0) = w;
+      }
+    if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_pp(const Fp8FwdArgs& a, hipStream_t s) {
+  constexpr int BLOCK_M = 256;
+  F8Params p;
+  p.q8 = a.q8;
+  p.k8 = a.k8;
+  p.v8t = a.v8t;
+  p.qs = a.q_scale;
+  p.ks = a.k_scale;
+  p.vs = a.v_scale;
+  p.o = static_cast<__bf16*>(a.o);
+  p.lse = a.lse;
+  p.H = a.H;
+  p.N = a.N;
+  p.nmb = (a.N + BLOCK_M - 1) / BLOCK_M;
+  p.total = a.B * a.H * p.nmb;
+  p.nblk = a.N / a.block_rows;
+  p.scale_log2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((attn_fwd_fp8_pp_kernel<D, CAUSAL>), dim3(p.total), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, int BN, bool CAUSAL>
 hipError_t launch_one(const Fp8FwdArgs& a, hipStream_t s) {
   constexpr int BLOCK_M = 128;
@@ -358,8 +668,8 @@ hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* su
     return hipSuccess;
   }
   switch (a.d) {
-    case 64: return launch_mask<64, 128>(a, stream);
-    case 128: return launch_mask<128, 128>(a, stream);
+    case 64: return a.causal ? launch_pp<64, true>(a, stream) : launch_pp<64, false>(a, stream);
+    case 128: return a.causal ? launch_pp<128, true>(a, stream) : launch_pp<128, false>(a, stream);
     case 256: return launch_mask<256, 64>(a, stream);
   }
   *supported = false;
