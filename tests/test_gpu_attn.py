@@ -171,3 +171,42 @@ def test_softmax_invariants_on_gpu():
     pref = np.cumsum(to_f64(v2[0, 0]), 0) / np.arange(1, N + 1)[:, None]
     assert np.abs(to_f64(o[0, 0]) - pref).max() <= 2e-2
     np.testing.assert_allclose(lse[0, 0].cpu().double().numpy(), np.log(np.arange(1, N + 1)), atol=1e-4)
+
+
+def test_lse_split_merge_on_gpu():
+    # attention over the two halves of K/V, merged through their LSEs, equals
+    # attention over all keys (non-causal): checks the GPU's LSE as a quantity
+    B, H, N, d = 1, 2, 1000, 128
+    inp = make_inputs(B, H, N, d, "bf16", seed=41)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    half = 437
+    o, lse = attn_fwd(q, k, v)
+    o1, l1 = attn_fwd(q, k[:, :, :half].contiguous(), v[:, :, :half].contiguous())
+    o2, l2 = attn_fwd(q, k[:, :, half:].contiguous(), v[:, :, half:].contiguous())
+    torch.cuda.synchronize()
+    l1, l2 = l1.double().cpu(), l2.double().cpu()
+    lm = torch.logaddexp(l1, l2)
+    om = (torch.exp(l1 - lm)[..., None] * o1.double().cpu() + torch.exp(l2 - lm)[..., None] * o2.double().cpu())
+    assert (lse.double().cpu() - lm).abs().max().item() <= 1e-3
+    assert (o.double().cpu() - om).abs().max().item() <= 2e-2
+    o_ref, lse_ref = oracle.attention(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), 1 / math.sqrt(d), False)
+    assert np.abs(lm.numpy() - lse_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_rescale_every_tile(dtype, causal):
+    # scores grow steadily along the keys, so the running max moves by far more
+    # than the lazy-rescale threshold at every tile (the rescale path runs
+    # throughout); O and LSE must still match the oracle
+    B, H, N, d = 1, 2, 700, 128
+    g = torch.Generator().manual_seed(17)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = (u * 6.0 + 0.1 * torch.randn(B, H, N, d, generator=g))
+    ramp = torch.linspace(0.0, 200.0, N)[None, None, :, None]   # ~14 log2 units of score per 64 keys
+    k = ramp * u + 0.5 * torch.randn(B, H, N, d, generator=g)
+    v = torch.randn(B, H, N, d, generator=g)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    inp = {"q": q.to(tdt), "k": k.to(tdt), "v": v.to(tdt)}
+    _full_compare(inp, causal, tdt, f"rising scores {dtype} causal={causal}")
