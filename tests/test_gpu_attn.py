@@ -174,23 +174,30 @@ def test_softmax_invariants_on_gpu():
 
 
 def test_lse_split_merge_on_gpu():
-    # attention over the two halves of K/V, merged through their LSEs, equals
-    # attention over all keys (non-causal): checks the GPU's LSE as a quantity
-    B, H, N, d = 1, 2, 1000, 128
-    inp = make_inputs(B, H, N, d, "bf16", seed=41)
-    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
-    half = 437
-    o, lse = attn_fwd(q, k, v)
-    o1, l1 = attn_fwd(q, k[:, :, :half].contiguous(), v[:, :, :half].contiguous())
-    o2, l2 = attn_fwd(q, k[:, :, half:].contiguous(), v[:, :, half:].contiguous())
+    # attention of N queries over key sets A and B (N keys each), merged
+    # through the two LSEs, equals attention over the 2N keys [A; B] (run with
+    # the queries repeated to 2N rows, as the API takes N_q = N_k): checks the
+    # GPU's LSE as a quantity, not only against the oracle
+    B, H, N, d = 1, 2, 500, 128
+    inp_a = make_inputs(B, H, N, d, "bf16", seed=41)
+    inp_b = make_inputs(B, H, N, d, "bf16", seed=42)
+    q = inp_a["q"].cuda()
+    ka, va = inp_a["k"].cuda(), inp_a["v"].cuda()
+    kb, vb = inp_b["k"].cuda(), inp_b["v"].cuda()
+    o1, l1 = attn_fwd(q, ka, va)
+    o2, l2 = attn_fwd(q, kb, vb)
+    o, lse = attn_fwd(torch.cat([q, q], 2), torch.cat([ka, kb], 2), torch.cat([va, vb], 2))
     torch.cuda.synchronize()
     l1, l2 = l1.double().cpu(), l2.double().cpu()
     lm = torch.logaddexp(l1, l2)
-    om = (torch.exp(l1 - lm)[..., None] * o1.double().cpu() + torch.exp(l2 - lm)[..., None] * o2.double().cpu())
-    assert (lse.double().cpu() - lm).abs().max().item() <= 1e-3
-    assert (o.double().cpu() - om).abs().max().item() <= 2e-2
-    o_ref, lse_ref = oracle.attention(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), 1 / math.sqrt(d), False)
-    assert np.abs(lm.numpy() - lse_ref).max() <= 1e-3
+    om = torch.exp(l1 - lm)[..., None] * o1.double().cpu() + torch.exp(l2 - lm)[..., None] * o2.double().cpu()
+    assert (lse[:, :, :N].double().cpu() - lm).abs().max().item() <= 1e-3
+    assert (o[:, :, :N].double().cpu() - om).abs().max().item() <= 2e-2
+    kk = np.concatenate([to_f64(inp_a["k"]), to_f64(inp_b["k"])], 2)
+    vv = np.concatenate([to_f64(inp_a["v"]), to_f64(inp_b["v"])], 2)
+    qq = np.concatenate([to_f64(inp_a["q"])] * 2, 2)
+    _, lse_ref = oracle.attention(qq, kk, vv, 1 / math.sqrt(d), False)
+    assert np.abs(lm.numpy() - lse_ref[:, :, :N]).max() <= 1e-3
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
