@@ -17,8 +17,14 @@
 //    (sV_j the tile's V block scale, sVmax the largest V block scale of the
 //    head); the factor enters the exp2 argument as a per-row bias, keeps
 //    P' <= 256 < 448 (no saturation) and keeps values down to 2^-10 of the
-//    row maximum out of the E4M3 subnormals; the row sums are kept from the
-//    unrounded P.  At the end O = acc * sVmax / 16 / l.
+//    row maximum out of the E4M3 subnormals.  At the end
+//    O = acc * sVmax / 16 / l.
+//  * Row sums l add up the E4M3-rounded P' (over the tile's gain), so O is
+//    normalised by exactly the weights its second product used (rows of the
+//    effective P sum to 1) and the LSE is the log of that normaliser.  The
+//    ping-pong kernel (d = 64, 128) forms them with two extra MFMAs per tile
+//    against an all-ones operand; the d = 256 kernel decodes the packed
+//    codes back to fp32 and adds them on the VALU.
 //  * The S^T rows are permuted so that each lane group holds 16 CONSECUTIVE
 //    keys of a 32-key block; the 32 P^T bytes a lane feeds to one PV MFMA
 //    then pair with two 16-byte LDS reads of V8t.
@@ -250,22 +256,15 @@ void attn_fwd_fp8_kernel(F8Params p) {
     // e = P * kPGain * fv  with P = exp2(s c - m_use)
     const float lg = __builtin_amdgcn_logf(kPGain * fv);   // v_log_f32 is log2
     const float bias = lg - m_use;
-    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, bias));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, bias));
-        sacc[kb][i] = e0;
-        sacc[kb][i + 1] = e1;
-        rs0 += e0;
-        rs1 += e1;
-      }
-    l_run += (rs0 + rs1) * (1.f / (kPGain * fv));
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, bias));
 
-    // P^T operands: slot s of lane group g <-> key 64 t + 32 (s / 16) + 16 g + s % 16
+    // P^T operands: slot s of lane group g <-> key 64 t + 32 (s / 16) + 16 g + s % 16.
+    // The row sums add up the rounded P' (decoded back from the codes).
     i32x8_t pf[NPV];
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int t = 0; t < NPV; ++t)
 #pragma unroll
@@ -274,7 +273,12 @@ void attn_fwd_fp8_kernel(F8Params p) {
         const int i0 = (w & 3) * 4;
         unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][i0], sacc[kb][i0 + 1], 0, false);
         pf[t][w] = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][i0 + 2], sacc[kb][i0 + 3], lo, true);
+        const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(pf[t][w], false);
+        const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(pf[t][w], true);
+        rs0 += r01[0] + r23[0];
+        rs1 += r01[1] + r23[1];
       }
+    l_run += (rs0 + rs1) * (1.f / (kPGain * fv));
 
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -328,7 +332,10 @@ void attn_fwd_fp8_kernel(F8Params p) {
 // SIMD; waves 0-3 and 4-7 alternate, one phase apart, between an MFMA phase
 // (S_j^T = K8_j Q8^T and O^T += V8_{j-1}^T P8_{j-1}^T) and a softmax phase
 // (mask, scale, row max, lazy rescale, P' = exp2(s c + bias) rounded to
-// E4M3, row sums), with a workgroup barrier between phases.  Every wave's 32
+// E4M3), with a workgroup barrier between phases.  The MFMA phase also forms
+// the row sums of the previous tile's rounded P' (ones x P'^T); the next
+// softmax phase adds them, divided by that tile's gain, to l before its own
+// rescale, as they are relative to the same running max.  Every wave's 32
 // rows lie inside one 128-row Q scale block; a 128-key tile is one K and one
 // V scale block.  K8 and V8t tiles are copied by waves 4-7 at the start of
 // their softmax phases, two phases ahead, into two stage objects each.
@@ -456,6 +463,16 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   for (int t = 0; t < NPV; ++t)
 #pragma unroll
     for (int w = 0; w < 8; ++w) pf[t][w] = 0;
+  // row sums of P' by MFMA: E4M3 ones (0x38) as the A operand; every row of
+  // the 32x32 result holds the column (query) sums of the P' in pf, over all
+  // 64 keys of each product, so l_run is the full row sum in both lane groups
+  i32x8_t ones;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;
+  f32x16_t lacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+  float inv_gain_prev = 0.f;     // 1 / (kPGain * fv) of the tile whose P' is in pf
 
   // MFMA phase: S^T of tile j and O^T += V^T P^T of tile j-1, operands read
   // LA MFMA pairs ahead; pair i = S block i % NKB, K-step i / NKB and O block
@@ -482,6 +499,14 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
       oacc[i % NDB] = mfma_fp8(vf[i], pf[i / NDB], oacc[i % NDB]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    {
+      f32x16_t z;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] = 0.f;
+      lacc = mfma_fp8(ones, pf[0], z);
+#pragma unroll
+      for (int t = 1; t < NPV; ++t) lacc = mfma_fp8(ones, pf[t], lacc);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -505,6 +530,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     const float m_tile = pair_max(mx) * c;
+    l_run = fmaf(lacc[0], inv_gain_prev, l_run);   // previous tile, same m_run as its P'
     if (__any(m_tile > m_run + kTau8)) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
@@ -517,7 +543,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float bias = __builtin_amdgcn_logf(kPGain * fv) - m_use;   // v_log_f32 is log2
-    float rs0 = 0.f, rs1 = 0.f;
+    inv_gain_prev = 1.f / (kPGain * fv);
 #pragma unroll
     for (int t = 0; t < NPV; ++t)
 #pragma unroll
@@ -528,12 +554,9 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
         const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0 + 1], c, bias));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0 + 2], c, bias));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i0 + 3], c, bias));
-        const unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        const unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pf[t][w], false);
         pf[t][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, lo, true);
-        rs0 += e0 + e2;
-        rs1 += e1 + e3;
       }
-    l_run += (rs0 + rs1) * (1.f / (kPGain * fv));
   };
 
   // pair j = K8 tile j (j < n_tiles) and V8t tile j-1 (j >= 1), into stage ST
@@ -588,8 +611,9 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   phase_barrier8();
   if (group == 0) run(ic8<0>{});
   else run(ic8<1>{});
+  l_run = fmaf(lacc[0], inv_gain_prev, l_run);   // the last tile
 
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = l_run;
   if (q_row < N) {
     const float inv = l_tot > 0.f ? svmax * (1.f / kPGain) / l_tot : 0.f;
     __bf16* orow = p.o + ((int64_t)bh * N + q_row) * D;

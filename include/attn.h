@@ -144,7 +144,12 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  * and O += P V where P is rounded to E4M3 after multiplication by a gain
  * of 16 * sV_j / max_j sV_j (sV_j the scale of V's key block j), so that
  * the V block scales fold into P and the lazy rescale threshold of 2^4
- * keeps the scaled P at most 256; the row sums use the unrounded fp32 P.
+ * keeps the scaled P at most 256.  The row sums l are those of the rounded
+ * P (each tile's sum divided by its gain), so O is normalised by exactly the
+ * weights its second product used, and lse is m + log(l) of that
+ * normaliser: it lies within log(1 + 2^-4) of the logsumexp of the
+ * dequantised scores (E4M3 keeps 3 mantissa bits) for rows whose scaled P
+ * stay in the E4M3 normal range.
  */
 int attn_fwd_fp8(int B, int H, int N, int d,
                  const uint8_t* q8, const float* q_scale,

@@ -154,8 +154,9 @@ def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
     2. Block-quantise Q~, K~ and V and dequantise them.
     3. Evaluate the exact definition on the dequantised values.  With
        quantize_p, P is additionally rounded as E4M3(P * p_gain) / p_gain
-       before the product with V, while the row sums stay unquantised --
-       the kernel's own choice for its second product.
+       and the rounded P serves both the product with V and the row sums
+       (the reading in which O is normalised by the weights it used; the
+       pages leave the precision of P's second product open).
     Returns fp64 (O, LSE).
     """
     qh = dequantize(*hadamard_rotate_quant(q, signs, block_rows)[:2], block_rows)
@@ -174,8 +175,8 @@ def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
             s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
         m = s.max(1)
         e = np.exp(s - m[:, None])
-        l = e.sum(1)
         eq = e4m3_decode(e4m3_encode(e * p_gain)) / p_gain
+        l = eq.sum(1)
         o[h] = (eq @ vf[h]) / l[:, None]
         lse[h] = m + np.log(l)
     return o.reshape(*lead, n, -1), lse.reshape(*lead, n)

@@ -237,8 +237,28 @@ def test_fp8_simulation_error_is_small_but_nonzero():
     err = oracle.rel_rms(o_sim, o_ex)
     # E4M3 keeps 3 mantissa bits: per-value relative error ~2-3 %.
     assert 0.005 < err < 0.1
-    o_p, _ = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, quantize_p=True)
+    o_p, lse_p = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, quantize_p=True)
     assert 0 < oracle.rel_rms(o_p, o_sim) < 0.06
+    # rounded P in the row sums: l moves by at most the E4M3 relative rounding
+    # (2^-4 for values in the normal range, which p_gain = 256 keeps the row
+    # maximum and everything within 2^-14 of it in)
+    _, lse_sim = oracle.attention_fp8_simulated(q, k, v, signs, 0.125)
+    dl = np.abs(lse_p - lse_sim)
+    assert 0 < dl.max() <= np.log1p(2.0 ** -4)
+
+
+def test_fp8_simulation_quantized_p_keeps_constant_v():
+    # with the rounded P in both the numerator and the row sums, the output is
+    # a convex combination of V rows: a constant V comes out unchanged (V's
+    # codes are all 448 and its scale |c| / 448, so V dequantises exactly)
+    B, H, N, d = 1, 2, 200, 64
+    rng = np.random.default_rng(11)
+    q, k = (rng.standard_normal((B, H, N, d)) * 3 for _ in range(2))
+    v = np.full((B, H, N, d), -1.75)
+    signs = rng.integers(0, 2, d) * 2 - 1
+    for causal in (False, True):
+        o_p, _ = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, causal=causal, quantize_p=True)
+        np.testing.assert_allclose(o_p, v, rtol=1e-13, atol=0)
 
 
 def test_rel_rms():
