@@ -337,8 +337,12 @@ void attn_fwd_fp8_kernel(F8Params p) {
 // softmax phase adds them, divided by that tile's gain, to l before its own
 // rescale, as they are relative to the same running max.  Every wave's 32
 // rows lie inside one 128-row Q scale block; a 128-key tile is one K and one
-// V scale block.  K8 and V8t tiles are copied by waves 4-7 at the start of
-// their softmax phases, two phases ahead, into two stage objects each.
+// V scale block.  K8 and V8t tiles are copied by waves 0-3 at the start of
+// their MFMA phases, two phases ahead, into two stage objects each: the
+// softmax phase is the longer of the two here (64 scores per lane and tile),
+// and an LDS-DMA instruction holds its issuing wave until the CU's address
+// unit accepts it (about 256 cycles for a 32 KiB pair), which the MFMA phase
+// absorbs in its wait at the barrier.
 
 __device__ __forceinline__ void phase_barrier8() {
   asm volatile("" ::: "memory");
@@ -389,8 +393,12 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   const int wq0 = m0 + wave * 32;
   const int q_row = wq0 + n;
   const int64_t head = (int64_t)bh * N * D;
-  const float* ksc = p.ks + (int64_t)bh * p.nblk;
-  const float* vsc = p.vs + (int64_t)bh * p.nblk;
+  // block scales through the constant address space: read-only for the
+  // kernel's lifetime, so uniform reads become scalar loads, which wait on
+  // their own counter instead of queueing behind the K/V copies
+  typedef __attribute__((address_space(4))) const float cfloat_t;
+  cfloat_t* ksc = (cfloat_t*)(p.ks + (int64_t)bh * p.nblk);
+  cfloat_t* vsc = (cfloat_t*)(p.vs + (int64_t)bh * p.nblk);
   const float sq = (wq0 < N) ? p.qs[(int64_t)bh * p.nblk + (wq0 >> 7)] : 1.f;
 
   float svmax = 0.f;
@@ -412,7 +420,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     }
   }
 
-  // copies by the 256 threads of group 1
+  // copies by the 256 threads of group 0
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + head), (short)0, N * D, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -510,11 +518,21 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // K and V block scales of the next softmax phase's tile, loaded a phase
+  // ahead: loaded in the phase that uses them, the wave would wait out the L2
+  // latency, which the K/V copies in flight raise to several hundred cycles
+  float ks_next = ksc[0], vs_next = vsc[0];
+
   // softmax phase of tile j (this wave needs it)
   auto phase_softmax = [&](int j) __attribute__((always_inline)) {
     const int kt0 = j * BN;
-    const float c = c0 * ksc[j];
-    const float fv = vsc[j] * inv_svmax;     // in (0, 1]
+    const float c = c0 * ks_next;
+    const float fv = vs_next * inv_svmax;     // in (0, 1]
+    {
+      const int jn = j + 1 < w_tiles ? j + 1 : j;
+      ks_next = ksc[jn];
+      vs_next = vsc[jn];
+    }
     if (CAUSAL && kt0 + BN - 1 > wq0) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -543,7 +561,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float bias = __builtin_amdgcn_logf(kPGain * fv) - m_use;   // v_log_f32 is log2
-    inv_gain_prev = 1.f / (kPGain * fv);
+    inv_gain_prev = __builtin_amdgcn_rcpf(kPGain * fv);
 #pragma unroll
     for (int t = 0; t < NPV; ++t)
 #pragma unroll
@@ -568,13 +586,13 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
 
   // Phase t (t % 4 == TM) of group G: local phase u = t - G; even u = MFMA
   // phase A_{u/2} reading pair u/2 from stage (u/2) & 1, odd u = softmax
-  // phase B_{(u-1)/2}.  Pair j is copied during phase 2j-2 (by group 1) and
+  // phase B_{(u-1)/2}.  Pair j is copied during phase 2j-2 (by group 0) and
   // waited for at the end of phase 2j-1.
   auto run = [&](auto g_c) __attribute__((always_inline)) {
     constexpr int G = decltype(g_c)::value;
     auto phase = [&](int t, auto tm_c) __attribute__((always_inline)) {
       constexpr int TM = decltype(tm_c)::value;
-      if constexpr ((TM & 1) == 0 && G == 1) {
+      if constexpr ((TM & 1) == 0 && G == 0) {
         const int j = t / 2 + 1;
         if (j <= n_tiles) copy_pair(j, ic8<(TM == 0) ? 1 : 0>{});
       }
@@ -603,7 +621,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     }
   };
 
-  if (group == 1) copy_pair(0, ic8<0>{});
+  if (group == 0) copy_pair(0, ic8<0>{});
 #pragma unroll
   for (int c = 0; c < V_BYTES / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
   wait_vmem();
