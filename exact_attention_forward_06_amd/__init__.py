@@ -8,8 +8,12 @@ Public API (thin wrappers over the C ABI of libattn.so, include/attn.h):
     attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False)
         -> (o, lse)
     attn_fwd_fp8_e2e(q, k, v, signs, causal=False) -> (o, lse)
+    attn_fwd_splitkv(q, k, v, num_splits, causal=False)
+        -> (o, lse, o_part, lse_part)
+    attn_merge(o_part, lse_part, out_dtype) -> (o, lse)
 """
-from ._lib import AttnError, attn_fwd, attn_fwd_fp8, hadamard_rotate_quant, load
+from ._lib import (AttnError, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_merge, hadamard_rotate_quant,
+                   load, splitkv_chunk)
 
 
 def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=None):
@@ -22,5 +26,5 @@ def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=No
                         stream=stream)
 
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "hadamard_rotate_quant",
-           "load"]
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
+           "hadamard_rotate_quant", "load", "splitkv_chunk"]

@@ -31,6 +31,9 @@ _SIGNATURES = {
     "hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp], _i),
     "attn_fwd_fp8": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, ctypes.c_float,
                       _i, _vp], _i),
+    "attn_fwd_splitkv": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                          ctypes.c_float, _i, _vp], _i),
+    "attn_merge": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
 }
 
 _lib = None
@@ -103,6 +106,59 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, retu
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides,
                         _ptr(out), _ptr(lse), scale, int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def splitkv_chunk(N: int, num_splits: int) -> int:
+    """Keys per range of attn_fwd_splitkv (attn_splitkv_chunk in attn.h)."""
+    per = -(-N // num_splits)
+    return -(-per // 128) * 128
+
+
+def attn_fwd_splitkv(q, k, v, num_splits, causal=False, softmax_scale=None, out=None, lse=None,
+                     o_part=None, lse_part=None, stream=None):
+    """attn_fwd as num_splits key-range partials plus their merge (fp16 /
+    bf16, d = 64 or 128).  Returns (o, lse, o_part, lse_part); the partial
+    buffers (fp32 [S, B, H, N, d] and [S, B, H, N]) are allocated unless
+    given."""
+    lib = load()
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype among fp32, fp16, bf16")
+    B, H, N, d = q.shape
+    strides = _bhnd_strides(q, k, v)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if o_part is None:
+        o_part = torch.empty((num_splits, B, H, N, d), dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, B, H, N), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_splitkv(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides,
+                                int(num_splits), _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
+                                scale, int(bool(causal)), _stream(stream)))
+    return out, lse, o_part, lse_part
+
+
+def attn_merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None, stream=None):
+    """Merge S partials (o_part fp32 [S, B, H, N, d], lse_part fp32
+    [S, B, H, N]) into (o [B, H, N, d] of out_dtype, lse fp32 [B, H, N])."""
+    lib = load()
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("partials must be fp32")
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    S, B, H, N, d = o_part.shape
+    if tuple(lse_part.shape) != (S, B, H, N):
+        raise ValueError("lse_part must be [S, B, H, N]")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+    _check(lib.attn_merge(_DTYPE_CODE[out.dtype], S, B, H, N, d, _ptr(o_part), _ptr(lse_part), _ptr(out),
+                          _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -183,6 +183,116 @@ int attn_fwd(int dtype, int B, int H, int N, int d, const void* q, const void* k
   return hip_status(e, "attn_fwd launch");
 }
 
+int attn_fwd_splitkv(int dtype, int B, int H, int N, int d, const void* q, const void* k,
+                     const void* v, const int64_t* qkv_strides, int num_splits, float* o_part,
+                     float* lse_part, void* o, float* lse, float softmax_scale, int causal,
+                     void* stream) {
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (int st = check_scale_causal(softmax_scale, causal)) return st;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "num_splits must be in 1..%d", ATTN_MAX_SPLITS);
+  if (dtype == ATTN_F32 || d == 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv covers fp16 / bf16 with d = 64 or 128");
+  int64_t sb, sh, sn;
+  strides_or_contiguous(qkv_strides, H, N, d, &sb, &sh, &sn);
+  const int64_t rows = (int64_t)B * H * N;
+  Span sq, sk, sv, so, sl{0, 0}, sp, spl;
+  if (int st = check_strided("q", q, B, H, N, d, sb, sh, sn, es, &sq)) return st;
+  if (int st = check_strided("k", k, B, H, N, d, sb, sh, sn, es, &sk)) return st;
+  if (int st = check_strided("v", v, B, H, N, d, sb, sh, sn, es, &sv)) return st;
+  if (int st = check_dense("o", o, rows * d * es, &so)) return st;
+  if (lse) {
+    if (int st = check_dense("lse", lse, rows * 4, &sl, false)) return st;
+  }
+  if (int st = check_dense("o_part", o_part, (int64_t)num_splits * rows * d * 4, &sp)) return st;
+  if (int st = check_dense("lse_part", lse_part, (int64_t)num_splits * rows * 4, &spl, false)) return st;
+  const Span ins[3] = {sq, sk, sv};
+  for (const Span& i : ins) {
+    if (overlaps(so, i) || overlaps(sp, i) || overlaps(spl, i) || (lse && overlaps(sl, i)))
+      return fail(ATTN_ERR_INVALID_ARGUMENT, "an output overlaps an input");
+  }
+  if (overlaps(so, sp) || overlaps(so, spl) || overlaps(sp, spl) ||
+      (lse && (overlaps(sl, so) || overlaps(sl, sp) || overlaps(sl, spl))))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs overlap each other");
+  if (((int64_t)N + 256) * sn * es + (int64_t)d * es >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
+
+  attn::FwdArgs a;
+  a.dtype = static_cast<attn::Dtype>(dtype);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.o = o;
+  a.lse = lse;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.nsplit = num_splits;
+  a.chunk = attn_splitkv_chunk(N, num_splits);
+  attn::MergeArgs m;
+  m.out_dtype = a.dtype;
+  m.S = num_splits;
+  m.B = B;
+  m.H = H;
+  m.N = N;
+  m.d = d;
+  m.o_part = o_part;
+  m.lse_part = lse_part;
+  m.o = o;
+  m.lse = lse;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  bool supported = true;
+  hipError_t e = attn::launch_attn_fwd16_pp_split(a, hs, &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no split-KV kernel for dtype %d d=%d", dtype, d);
+  if (e != hipSuccess) return hip_status(e, "attn_fwd_splitkv launch");
+  e = attn::launch_attn_merge(m, hs, &supported);
+  return hip_status(e, "attn_fwd_splitkv merge launch");
+}
+
+int attn_merge(int out_dtype, int S, int B, int H, int N, int d, const float* o_part,
+               const float* lse_part, void* o, float* lse, void* stream) {
+  const int es = elem_size(out_dtype);
+  if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", out_dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (S < 1 || S > ATTN_MAX_MERGE)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "S must be in 1..%d", ATTN_MAX_MERGE);
+  const int64_t rows = (int64_t)B * H * N;
+  Span sp, spl, so, sl{0, 0};
+  if (int st = check_dense("o_part", o_part, (int64_t)S * rows * d * 4, &sp)) return st;
+  if (int st = check_dense("lse_part", lse_part, (int64_t)S * rows * 4, &spl, false)) return st;
+  if (int st = check_dense("o", o, rows * d * es, &so)) return st;
+  if (lse) {
+    if (int st = check_dense("lse", lse, rows * 4, &sl, false)) return st;
+  }
+  if (overlaps(so, sp) || overlaps(so, spl) || (lse && (overlaps(sl, sp) || overlaps(sl, spl) || overlaps(sl, so))))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "an output overlaps an input or the other output");
+  attn::MergeArgs m;
+  m.out_dtype = static_cast<attn::Dtype>(out_dtype);
+  m.S = S;
+  m.B = B;
+  m.H = H;
+  m.N = N;
+  m.d = d;
+  m.o_part = o_part;
+  m.lse_part = lse_part;
+  m.o = o;
+  m.lse = lse;
+  bool supported = true;
+  hipError_t e = attn::launch_attn_merge(m, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_merge kernel for d=%d", d);
+  return hip_status(e, "attn_merge launch");
+}
+
 int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,
                           const int64_t* x_strides, const int8_t* signs, int block_rows,
                           int transpose_out, uint8_t* x8, float* scales, void* stream) {

@@ -32,6 +32,10 @@ struct Params {
   int64_t sb, sh, sn;   // element strides of q, k, v
   int H, N, nmb, total;
   float scale_log2;     // softmax_scale * log2(e)
+  // split-KV only: key range s covers keys [s * chunk, (s + 1) * chunk)
+  float* o_part;        // fp32 [nsplit, B, H, N, d], each range's normalised O
+  float* lse_part;      // fp32 [nsplit, B, H, N], each range's LSE (-inf if empty)
+  int nsplit, chunk, bh_count;
 };
 
 template <typename T>

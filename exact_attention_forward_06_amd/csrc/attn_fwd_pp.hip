@@ -63,7 +63,10 @@ __device__ __forceinline__ void phase_barrier() {
 // (simm16 = vmcnt 63 | expcnt 7 << 4 | lgkmcnt 0 << 8).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <typename T, int D, int BN, bool CAUSAL>
+// SPLIT: the grid also runs over p.nsplit key ranges; each workgroup covers
+// one range and writes that range's normalised O (fp32) and LSE to o_part
+// and lse_part, which attn_merge.hip combines.
+template <typename T, int D, int BN, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pp_kernel(Params p) {
   using Op = Ops<T>;
@@ -96,9 +99,19 @@ void attn_fwd_pp_kernel(Params p) {
   const int g = lane >> 5;
   const int N = p.N;
 
+  // work item -> (head, key range, Q block); the items of one head and range
+  // are consecutive, so they land on one XCD and share its L2
   const int logical = xcd_logical_id(blockIdx.x, p.total);
-  const int bh = logical / p.nmb;
-  int mb = logical - bh * p.nmb;
+  int bh, mb, split = 0;
+  if constexpr (SPLIT) {
+    bh = logical / (p.nmb * p.nsplit);
+    const int rem = logical - bh * p.nmb * p.nsplit;
+    split = rem / p.nmb;
+    mb = rem - split * p.nmb;
+  } else {
+    bh = logical / p.nmb;
+    mb = logical - bh * p.nmb;
+  }
   if (CAUSAL) mb = p.nmb - 1 - mb;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
@@ -165,16 +178,32 @@ void attn_fwd_pp_kernel(Params p) {
   float m_run = -INFINITY;   // running max of scale * log2(e) * s (possibly stale by < kTau)
   float l_run = 0.f;         // this lane's half of the running row sum
 
-  const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  // keys [k_lo, kv_end) of this item, in tiles j_base .. j_base + n_tiles - 1
+  const int k_lo = SPLIT ? split * p.chunk : 0;
+  int kv_end = SPLIT ? min(N, k_lo + p.chunk) : N;
+  if (CAUSAL) kv_end = min(kv_end, m0 + BLOCK_M);
+  const int j_base = k_lo / BN;            // chunk is a multiple of 128, and BN divides 128
+  const int n_tiles = kv_end > k_lo ? (kv_end - k_lo + BN - 1) / BN : 0;
   // tiles this wave needs (causal: keys up to its last row)
-  const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
+  const int w_tiles =
+      (wq0 >= N) ? 0 : (CAUSAL ? max(0, min(n_tiles, (wq0 + 31) / BN + 1 - j_base)) : n_tiles);
+  if constexpr (SPLIT) {
+    if (n_tiles == 0) {   // the whole range is masked for this Q block: O = 0, LSE = -inf
+      if (q_row < N) {
+        float* orow = p.o_part + (((int64_t)split * p.bh_count + bh) * N + q_row) * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) *(f32x4_t*)(orow + c * 8 + g * 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = -INFINITY;
+      }
+      return;
+    }
+  }
   const float c = p.scale_log2;
 
   f32x16_t sacc[NKB];
   frag pf[NCC];
 
-  auto tile_max = [&](int kt0) __attribute__((always_inline)) -> float {
+  auto tile_max = [&](int kt0) __attribute__((always_inline)) -> float {   // kt0: global key index
     const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
@@ -270,8 +299,8 @@ void attn_fwd_pp_kernel(Params p) {
   // pair j = K_j (j < n_tiles) and V_{j-1} (j >= 1), into stage ST
   auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
-    if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, j * BN * rbg, dma_off);
-    if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j - 1) * BN * rbg, dma_off);
+    if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
+    if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
   };
 
   // Phase t (t % 4 == TM) of group G.  Local phase u = t - G: even u = MFMA
@@ -301,7 +330,7 @@ void attn_fwd_pp_kernel(Params p) {
           // stage 0 is zero-filled, so O^T gains exactly zero.
           if (j <= w_tiles) phase_mfma(ic<1>{}, ic<1>{}, kst, vst);
         } else if (j < w_tiles) {
-          update_max(tile_max(j * BN));
+          update_max(tile_max((j_base + j) * BN));
           softmax_p();
         }
       }
@@ -331,6 +360,22 @@ void attn_fwd_pp_kernel(Params p) {
 
   // epilogue: O = O / l, LSE = m ln2 + ln l
   const float l_tot = pair_sum(l_run);
+  if constexpr (SPLIT) {
+    if (q_row < N) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* orow = p.o_part + (((int64_t)split * p.bh_count + bh) * N + q_row) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int d0 = db * 32 + t * 8 + g * 4;
+          *(f32x4_t*)(orow + d0) = f32x4_t{oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv,
+                                            oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv};
+        }
+      if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = m_run * kLn2 + logf(l_tot);
+    }
+    return;
+  }
   if (q_row < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     char* orow = p.o + (((int64_t)bh * N + q_row) * D) * 2;
@@ -347,7 +392,7 @@ void attn_fwd_pp_kernel(Params p) {
   }
 }
 
-template <typename T, int D, int BN, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL, bool SPLIT>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   constexpr int BLOCK_M = 256;
   Params p;
@@ -362,18 +407,23 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   p.H = a.H;
   p.N = a.N;
   p.nmb = (a.N + BLOCK_M - 1) / BLOCK_M;
-  p.total = a.B * a.H * p.nmb;
   p.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, BN, CAUSAL>), dim3(p.total), dim3(512), 0, stream, p);
+  p.bh_count = a.B * a.H;
+  p.nsplit = SPLIT ? a.nsplit : 1;
+  p.chunk = SPLIT ? a.chunk : a.N;
+  p.o_part = a.o_part;
+  p.lse_part = a.lse_part;
+  p.total = p.bh_count * p.nmb * p.nsplit;
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, BN, CAUSAL, SPLIT>), dim3(p.total), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SPLIT>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool* ok) {
   *ok = true;
   auto go = [&](auto dc, auto bnc) -> hipError_t {
     constexpr int D = decltype(dc)::value, BN = decltype(bnc)::value;
-    return a.causal ? launch_one<T, D, BN, true>(a, s) : launch_one<T, D, BN, false>(a, s);
+    return a.causal ? launch_one<T, D, BN, true, SPLIT>(a, s) : launch_one<T, D, BN, false, SPLIT>(a, s);
   };
   switch (a.d) {
     case 64: return go(ic<64>{}, ic<128>{});
@@ -388,8 +438,19 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool* ok) {
 // d = 64 and 128 in bf16 / fp16; `supported` is false for anything else.
 hipError_t launch_attn_fwd16_pp(const FwdArgs& a, hipStream_t stream, bool* supported) {
   switch (a.dtype) {
-    case Dtype::BF16: return launch_t<__bf16>(a, stream, supported);
-    case Dtype::F16: return launch_t<_Float16>(a, stream, supported);
+    case Dtype::BF16: return launch_t<__bf16, false>(a, stream, supported);
+    case Dtype::F16: return launch_t<_Float16, false>(a, stream, supported);
+    default: break;
+  }
+  *supported = false;
+  return hipSuccess;
+}
+
+// Split-KV: partial O / LSE per key range (a.nsplit ranges of a.chunk keys).
+hipError_t launch_attn_fwd16_pp_split(const FwdArgs& a, hipStream_t stream, bool* supported) {
+  switch (a.dtype) {
+    case Dtype::BF16: return launch_t<__bf16, true>(a, stream, supported);
+    case Dtype::F16: return launch_t<_Float16, true>(a, stream, supported);
     default: break;
   }
   *supported = false;

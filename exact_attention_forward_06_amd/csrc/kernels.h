@@ -19,6 +19,20 @@ struct FwdArgs {
   float* lse;           // [B, H, N] or nullptr
   float scale;          // softmax scale (> 0)
   bool causal;
+  // split-KV only (attn_fwd_splitkv): partial outputs of nsplit key ranges
+  float* o_part = nullptr;    // fp32 [nsplit, B, H, N, d]
+  float* lse_part = nullptr;  // fp32 [nsplit, B, H, N]
+  int nsplit = 1;
+  int chunk = 0;              // keys per range, a multiple of 128
+};
+
+struct MergeArgs {
+  Dtype out_dtype;
+  int S, B, H, N, d;
+  const float* o_part;        // fp32 [S, B, H, N, d]
+  const float* lse_part;      // fp32 [S, B, H, N]
+  void* o;                    // out_dtype [B, H, N, d]
+  float* lse;                 // [B, H, N] or nullptr
 };
 
 struct QuantArgs {
@@ -53,5 +67,8 @@ struct Fp8FwdArgs {
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* supported);
+// split-KV partials (bf16 / fp16, d = 64 and 128) and their merge
+hipError_t launch_attn_fwd16_pp_split(const FwdArgs& a, hipStream_t stream, bool* supported);
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream, bool* supported);
 
 }  // namespace attn

@@ -16,6 +16,9 @@ PCG64 stream, draw order Q, K, V, then the FP8 extras):
                    non-causal, seed 5; after V the generator draws the
                    outlier channel set (shared by Q and K, scaled x20
                    before the bf16 cast) and the +-1 sign vector D.
+  bf16_few_heads_8k  bf16, B=1 H=2 N=8192 d=128, non-causal, seed 9: a
+                   long sequence with few heads (64 Q blocks of 256 rows
+                   for 256 compute units), the split-KV case.
 
 The random sign diagonal is a random draw of the method (FlashAttention-3
 page, section on incoherent processing), so it is produced here and passed
@@ -63,6 +66,7 @@ WORKLOADS = {
         Workload("bf16_d64", "bf16", 8, 16, 4096, 64, False, 4),
         Workload("bf16_d256", "bf16", 4, 8, 4096, 256, False, 4),
         Workload("fp8_hadamard_8k", "fp8", 2, 16, 8192, 128, False, 5, outlier_frac=0.005),
+        Workload("bf16_few_heads_8k", "bf16", 1, 2, 8192, 128, False, 9),
     ]
 }
 

@@ -99,6 +99,76 @@ int attn_fwd(int dtype, int B, int H, int N, int d,
              float softmax_scale, int causal, void* stream);
 
 /*
+ * Split-KV: the key axis cut into ranges processed by separate workgroups
+ * (more parallelism than batch x heads x Q blocks gives, for few heads or
+ * long sequences: the sequence-parallel direction of the "FlashAttention-2/3"
+ * page, section "FlashAttention-2 的三大改进", 改进二), then merged exactly
+ * through each range's logsumexp (the stored LSE of the "Flash Attention V3"
+ * page, section 2.2).  The same merge combines partial results computed
+ * anywhere -- the building block that ring attention over several devices
+ * needs (same page as above, section "常见误读纠偏", 误读三).
+ *
+ * Range s of S covers keys [s * chunk, min(N, (s + 1) * chunk)) with
+ * chunk = attn_splitkv_chunk(N, S), i.e. ceil(N / S) rounded up to a
+ * multiple of 128; ranges past N (or fully masked for a row under the causal
+ * mask) carry O = 0 and LSE = -inf for that row.
+ */
+#define ATTN_MAX_SPLITS 64
+#define ATTN_MAX_MERGE 1024
+
+static inline int attn_splitkv_chunk(int N, int S) {
+  const int per = (N + S - 1) / S;
+  return (per + 127) / 128 * 128;
+}
+
+/*
+ * attn_fwd_splitkv -- attn_fwd computed as S key-range partials plus a merge.
+ *
+ *   dtype          ATTN_F16 or ATTN_BF16 (others: ATTN_ERR_UNSUPPORTED).
+ *   B, H, N, d     as in attn_fwd; d in {64, 128} (256: ATTN_ERR_UNSUPPORTED).
+ *   q, k, v, qkv_strides, softmax_scale, causal, stream   as in attn_fwd.
+ *   num_splits     S, 1 <= S <= ATTN_MAX_SPLITS.
+ *   o_part         device fp32 [S, B, H, N, d] workspace, written with each
+ *                  range's normalised output (16-byte aligned).
+ *   lse_part       device fp32 [S, B, H, N] workspace, each range's LSE.
+ *   o, lse         outputs as in attn_fwd (lse may be NULL).
+ *
+ * o_part and lse_part are caller-owned scratch that the call overwrites and
+ * the library does not keep; they must not overlap each other, the inputs
+ * or the outputs.  Both launches go on `stream` in order.  The result equals
+ * attn_fwd's up to fp32 rounding order (plus one fp32 rounding of each
+ * partial output).
+ */
+int attn_fwd_splitkv(int dtype, int B, int H, int N, int d,
+                     const void* q, const void* k, const void* v,
+                     const int64_t* qkv_strides, int num_splits,
+                     float* o_part, float* lse_part,
+                     void* o, float* lse,
+                     float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_merge -- combine S attention partials over disjoint key ranges:
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ *
+ *   out_dtype      ATTN_F32, ATTN_F16 or ATTN_BF16: type of o.
+ *   S              number of partials, 1 <= S <= ATTN_MAX_MERGE.
+ *   B, H, N, d     shape of each partial; d in {64, 128, 256}.
+ *   o_part         device fp32 [S, B, H, N, d]: each partial's output,
+ *                  normalised by its own row sum (16-byte aligned).
+ *   lse_part       device fp32 [S, B, H, N]: each partial's LSE, -inf for a
+ *                  row that saw no key in that range (weight 0).
+ *   o              device [B, H, N, d] output of out_dtype (contiguous).
+ *   lse            device fp32 [B, H, N] output, or NULL.
+ *   stream         hipStream_t or NULL.
+ *
+ * A row whose partials are all -inf gets O = 0 and LSE = -inf.  Outputs must
+ * not overlap the partials.
+ */
+int attn_merge(int out_dtype, int S, int B, int H, int N, int d,
+               const float* o_part, const float* lse_part,
+               void* o, float* lse, void* stream);
+
+/*
  * hadamard_rotate_quant -- FP8 pre-pass for one tensor.
  *
  * For every row x of x[B, H, N, d]: if `signs` is given, x~ = (1/sqrt(d)) H D x

@@ -113,6 +113,49 @@ def attention_rows(q, k, v, rows, scale, causal=False):
     return o, m + np.log(l)
 
 
+def attention_partial(q, k, v, scale, k_begin, k_end, causal=False):
+    """One head's attention restricted to the keys [k_begin, k_end): the
+    definition above with the score matrix cut to those columns (the causal
+    mask stays in global indices).  This is what a key range of split-KV
+    computes -- the sequence-parallel split of the "FlashAttention-2/3" page
+    (section "FlashAttention-2 的三大改进", 改进二), with the range's LSE as its
+    state ("Flash Attention V3" page, section 2.2).
+
+    Returns fp64 (O_part [N, d], LSE_part [N]); a row that sees no key of the
+    range gets O_part = 0 and LSE_part = -inf.
+    """
+    s = scores(q, k, scale, causal)[:, k_begin:k_end]
+    n = s.shape[0]
+    vr = _f64(v)[k_begin:k_end]
+    o = np.zeros((n, vr.shape[1]), np.float64)
+    lse = np.full(n, -np.inf)
+    seen = np.any(np.isfinite(s), axis=1) if s.shape[1] else np.zeros(n, bool)
+    if np.any(seen):
+        p, m, l = row_softmax(s[seen])
+        o[seen] = p @ vr
+        lse[seen] = m + np.log(l)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine partial results over disjoint key ranges:
+    LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the online
+    softmax update of the "FlashAttention-2/3" page, section "在线 Softmax",
+    applied to whole ranges).  o_parts [S, ..., N, d], lse_parts [S, ..., N];
+    rows whose partials are all -inf get O = 0 and LSE = -inf."""
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    m = np.max(lse_parts, axis=0)
+    seen = np.isfinite(m)
+    msafe = np.where(seen, m, 0.0)
+    w = np.exp(lse_parts - msafe[None])            # 0 for -inf partials
+    tot = np.sum(w, axis=0)
+    o = np.sum(w[..., None] * o_parts, axis=0) / np.where(seen, tot, 1.0)[..., None]
+    o = np.where(seen[..., None], o, 0.0)
+    lse = np.where(seen, msafe + np.log(np.where(seen, tot, 1.0)), -np.inf)
+    return o, lse
+
+
 def credited_flops(B, H, N, d, causal):
     """Throughput convention: 4*B*H*N^2*d, halved under the causal mask."""
     f = 4.0 * B * H * N * N * d

@@ -34,7 +34,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
-                          "hadamard_rotate_quant", "attn_fwd_fp8"}
+                          "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_abi_version() == 1
@@ -124,6 +124,59 @@ def _fp8(lib, B=1, H=1, N=256, d=128, q8=A, qs=A + 0x8000000, k8=B_, ks=B_ + 0x8
 def test_fp8_rejects(lib, kw, status, msg):
     assert _fp8(lib, **kw) == status
     assert msg in lib.attn_last_error().decode()
+
+
+OP = 0x80000000      # partial buffers: far from the inputs and outputs
+LP = 0xC0000000
+
+
+def _split(lib, dtype=2, B=1, H=1, N=256, d=128, q=A, k=B_, v=C, strides=None, S=4, op=OP, lp=LP, o=O,
+           lse=L, scale=0.088, causal=0):
+    s = None if strides is None else (ctypes.c_int64 * 3)(*strides)
+    return lib.attn_fwd_splitkv(dtype, B, H, N, d, q, k, v, s, S, op, lp, o, lse, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(op=None), 1, "o_part is NULL"),
+    (dict(lp=None), 1, "lse_part is NULL"),
+    (dict(S=0), 1, "num_splits"),
+    (dict(S=65), 1, "num_splits"),
+    (dict(dtype=0), 2, "fp16 / bf16"),
+    (dict(d=256), 2, "fp16 / bf16"),
+    (dict(d=40), 2, "head dimension"),
+    (dict(op=A), 1, "overlaps an input"),
+    (dict(lp=O), 1, "overlap each other"),
+    (dict(op=OP + 8), 1, "16-byte aligned"),
+    (dict(causal=3), 1, "causal"),
+])
+def test_splitkv_rejects(lib, kw, status, msg):
+    assert _split(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def _merge(lib, dtype=2, S=3, B=1, H=2, N=100, d=64, op=OP, lp=LP, o=O, lse=L):
+    return lib.attn_merge(dtype, S, B, H, N, d, op, lp, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(op=None), 1, "o_part is NULL"),
+    (dict(o=None), 1, "o is NULL"),
+    (dict(S=0), 1, "S must be"),
+    (dict(S=1025), 1, "S must be"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(dtype=5), 1, "unknown dtype"),
+    (dict(o=OP), 1, "overlaps"),
+    (dict(lse=LP + 16), 1, "overlaps"),
+])
+def test_merge_rejects(lib, kw, status, msg):
+    assert _merge(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_splitkv_chunk_rule():
+    assert [_lib.splitkv_chunk(n, s) for n, s in [(1, 1), (128, 1), (129, 1), (1000, 3), (8192, 4),
+                                                   (8192, 64), (300, 5)]] == [128, 128, 256, 384, 2048,
+                                                                              128, 128]
 
 
 def test_python_binding_refuses_missing_library(tmp_path):

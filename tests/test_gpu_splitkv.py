@@ -1,0 +1,110 @@
+"""GPU parity of split-KV attention (attn_fwd_splitkv) and of the partial
+merge (attn_merge) against the fp64 oracle.
+
+Tolerances: the merged O and LSE use attn_fwd's (bf16 / fp16 O: max |err|
+<= 2e-2, mean <= 2e-3; LSE: max |err| <= 1e-3).  Each range's partial O is
+fp32 (one rounding less than O) and is held to the same bar; a range a row
+cannot see must come back exactly as O = 0, LSE = -inf.  attn_merge with
+fp32 output on given partials: relative 1e-5 (fp32 exp and sums).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_forward_06_amd import attn_fwd_splitkv, attn_merge, splitkv_chunk
+from exact_attention_forward_06_amd.inputs import make_inputs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+_DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def _check(o_gpu, lse_gpu, o_ref, lse_ref, what):
+    err = np.abs(o_gpu - o_ref)
+    assert np.all(np.isfinite(o_gpu)), what
+    assert err.max() <= 2e-2, f"{what}: max |O err| {err.max():.3e}"
+    assert err.mean() <= 2e-3, f"{what}: mean |O err| {err.mean():.3e}"
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: -inf pattern of LSE"
+    if fin.any():
+        lerr = np.abs(lse_gpu[fin] - lse_ref[fin])
+        assert lerr.max() <= 1e-3, f"{what}: max |LSE err| {lerr.max():.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,S", [(300, 3), (512, 1), (1000, 7), (130, 2), (200, 64)])
+def test_splitkv_matches_oracle(dtype, d, causal, N, S):
+    """Merged output and every range's partial against the oracle; (200, 64)
+    leaves most ranges past N (empty), (130, 2) has a ragged last range."""
+    B, H = 1, 2
+    print(f"\n[splitkv] {dtype} d={d} causal={causal} N={N} S={S}", flush=True)
+    inp = make_inputs(B, H, N, d, dtype, seed=N + S + d)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o, lse, o_part, lse_part = attn_fwd_splitkv(q, k, v, S, causal=causal)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = (to_f64(inp[n]) for n in ("q", "k", "v"))
+    o_ref, lse_ref = oracle.attention(qd, kd, vd, scale, causal)
+    _check(to_f64(o), lse.cpu().double().numpy(), o_ref, lse_ref, "merged")
+    chunk = splitkv_chunk(N, S)
+    op = o_part.cpu().double().numpy()
+    lp = lse_part.cpu().double().numpy()
+    for s in range(S):
+        lo, hi = s * chunk, min(N, (s + 1) * chunk)
+        for h in range(H):
+            po, pl = oracle.attention_partial(qd[0, h], kd[0, h], vd[0, h], scale, min(lo, N), max(lo, hi), causal)
+            _check(op[s, 0, h], lp[s, 0, h], po, pl, f"range {s} head {h}")
+            unseen = ~np.isfinite(pl)
+            assert np.all(op[s, 0, h][unseen] == 0.0), f"range {s}: O of unseen rows must be 0"
+
+
+def test_splitkv_full_size_sampled_rows():
+    """A few-heads, long-sequence shape where one Q block per CU is all the
+    parallelism attn_fwd has (B=1, H=8, N=8192, d=128, 4 ranges): sampled
+    rows of every head against the oracle."""
+    B, H, N, d, S = 1, 8, 8192, 128, 4
+    inp = make_inputs(B, H, N, d, "bf16", seed=7)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    for causal in (False, True):
+        print(f"\n[splitkv full] causal={causal}", flush=True)
+        o, lse, _, _ = attn_fwd_splitkv(q, k, v, S, causal=causal)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(8)
+        for h in range(H):
+            rows = np.sort(rng.choice(N, 24, replace=False))
+            rows = np.unique(np.concatenate([rows, [0, 2047, 2048, N - 1]]))
+            o_ref, lse_ref = oracle.attention_rows(to_f64(inp["q"][0, h]), to_f64(inp["k"][0, h]),
+                                                   to_f64(inp["v"][0, h]), rows, 1 / math.sqrt(d), causal)
+            _check(to_f64(o[0, h].cpu())[rows], lse[0, h].cpu().double().numpy()[rows], o_ref, lse_ref,
+                   f"head {h}")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+def test_merge_matches_oracle(d, out):
+    """attn_merge on given partials, including a row no partial saw and
+    partials of very different magnitude."""
+    S, B, H, N = 5, 2, 3, 77
+    rng = np.random.default_rng(d)
+    o_parts = rng.standard_normal((S, B, H, N, d)).astype(np.float32)
+    lse_parts = (rng.standard_normal((S, B, H, N)) * 30).astype(np.float32)
+    lse_parts[:, 1, 2, 5] = -np.inf
+    lse_parts[2, 0, 0, :] = -np.inf
+    o_ref, lse_ref = oracle.merge_partials(o_parts.astype(np.float64), lse_parts.astype(np.float64))
+    dt = torch.float32 if out == "fp32" else torch.bfloat16
+    o, lse = attn_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda(), out_dtype=dt)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    assert lg[1, 2, 5] == -np.inf and np.all(og[1, 2, 5] == 0)
+    fin = np.isfinite(lse_ref)
+    np.testing.assert_allclose(lg[fin], lse_ref[fin], rtol=1e-6, atol=1e-5)
+    if out == "fp32":
+        np.testing.assert_allclose(og, o_ref, rtol=1e-5, atol=1e-5)
+    else:
+        np.testing.assert_allclose(og, o_ref, rtol=2 ** -8, atol=1e-3)

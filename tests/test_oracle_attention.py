@@ -234,6 +234,75 @@ def test_lse_split_merge():
     np.testing.assert_allclose(om, o, atol=1e-13)
 
 
+# ------------------------------------------------------ key-range partials
+def _brute_force_partial(q, k, v, scale, causal, k_begin, k_end):
+    """Pure-Python loops: softmax over the keys of [k_begin, k_end) that a
+    row sees; (0, -inf) for a row that sees none."""
+    o, lse = [], []
+    for i in range(len(q)):
+        keys = [j for j in range(k_begin, k_end) if not (causal and j > i)]
+        if not keys:
+            o.append([0.0] * len(v[0]))
+            lse.append(-math.inf)
+            continue
+        s = [scale * math.fsum(a * b for a, b in zip(q[i], k[j])) for j in keys]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = math.fsum(w)
+        o.append([math.fsum(w[t] * v[j][c] for t, j in enumerate(keys)) / tot for c in range(len(v[0]))])
+        lse.append(mx + math.log(tot))
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("rng_", [(0, 5), (3, 9), (6, 11), (11, 11)])
+def test_partial_matches_brute_force(causal, rng_):
+    n, d = 11, 4
+    q, k, v = _rand((n, d), 70), _rand((n, d), 71), _rand((n, d), 72)
+    o, lse = oracle.attention_partial(q, k, v, 0.6, rng_[0], rng_[1], causal)
+    ob, lb = _brute_force_partial(q.tolist(), k.tolist(), v.tolist(), 0.6, causal, *rng_)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    assert np.array_equal(np.isinf(lse), np.isinf(lb))
+    np.testing.assert_allclose(lse[np.isfinite(lb)], lb[np.isfinite(lb)], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_partials_over_a_partition_merge_to_attention(causal):
+    """Ranges that partition the keys (uneven, one past N, one empty) merge
+    back to the full result; a range a row cannot see carries (0, -inf)."""
+    n, d = 37, 6
+    q, k, v = _rand((n, d), 73), _rand((n, d), 74), _rand((n, d), 75)
+    cuts = [0, 5, 5, 19, 30, 40]
+    parts = [oracle.attention_partial(q, k, v, 0.4, a, b, causal) for a, b in zip(cuts, cuts[1:])]
+    o, lse = oracle.merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    oe, le = attention_head(q, k, v, 0.4, causal)
+    np.testing.assert_allclose(o, oe, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, le, rtol=0, atol=1e-13)
+    assert np.all(parts[1][1] == -np.inf) and np.all(parts[1][0] == 0)   # the empty range [5, 5)
+    if causal:                                                            # rows 0..18 cannot see [19, 30)
+        assert np.all(parts[3][1][:19] == -np.inf) and np.all(parts[3][0][:19] == 0)
+
+
+def test_merge_is_associative_and_handles_all_empty_rows():
+    rng = np.random.default_rng(76)
+    o_parts = rng.standard_normal((3, 2, 5, 4))
+    lse_parts = rng.standard_normal((3, 2, 5)) * 3
+    lse_parts[:, 1, 2] = -np.inf          # a row no range saw
+    lse_parts[0, 0, 0] = -np.inf          # a row one range did not see
+    o, lse = oracle.merge_partials(o_parts, lse_parts)
+    o12, l12 = oracle.merge_partials(o_parts[:2], lse_parts[:2])
+    o3, l3 = oracle.merge_partials(np.stack([o12, o_parts[2]]), np.stack([l12, lse_parts[2]]))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(o3, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l3[fin], lse[fin], rtol=0, atol=1e-13)
+    assert lse[1, 2] == -np.inf and np.all(o[1, 2] == 0)
+    # a single partial merges to itself
+    o1, l1 = oracle.merge_partials(o_parts[:1], lse_parts[:1])
+    f1 = np.isfinite(lse_parts[0])
+    np.testing.assert_allclose(o1[f1], o_parts[0][f1], atol=1e-15)
+    assert np.all(o1[~f1] == 0) and np.all(l1[~f1] == -np.inf)
+
+
 def test_rows_subset_equals_full():
     n, d = 50, 8
     q, k, v = _rand((n, d), 60), _rand((n, d), 61), _rand((n, d), 62)
