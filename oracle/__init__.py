@@ -6,14 +6,14 @@ no code with it (only the seeded input generator serves both).
 """
 from .attention import (attention, attention_head, attention_partial, attention_rows, credited_flops,
                         merge_partials, row_softmax, scores)
-from .fp8 import (E4M3_MAX, attention_fp8_simulated, block_quantize, dequantize,
-                  e4m3_decode, e4m3_encode, hadamard_rotate_quant, rel_rms, rotate,
+from .fp8 import (E4M3_MAX, E5M2_MAX, FORMATS, attention_fp8_simulated, block_quantize, dequantize,
+                  e4m3_decode, e4m3_encode, e5m2_decode, e5m2_encode, hadamard_rotate_quant, rel_rms, rotate,
                   sylvester_hadamard)
 
 __all__ = [
     "attention", "attention_head", "attention_partial", "attention_rows", "credited_flops",
     "merge_partials", "row_softmax",
-    "scores", "E4M3_MAX", "attention_fp8_simulated", "block_quantize", "dequantize",
-    "e4m3_decode", "e4m3_encode", "hadamard_rotate_quant", "rel_rms", "rotate",
+    "scores", "E4M3_MAX", "E5M2_MAX", "FORMATS", "attention_fp8_simulated", "block_quantize",
+    "dequantize", "e4m3_decode", "e4m3_encode", "e5m2_decode", "e5m2_encode", "hadamard_rotate_quant", "rel_rms", "rotate",
     "sylvester_hadamard",
 ]

@@ -27,6 +27,11 @@ Sources and readings:
     its definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
     bits, subnormals m * 2^-9, no infinities, S.1111.111 is NaN, largest
     finite value 448.
+  * E5M2, the other format that page names: the OCP E5M2 encoding, from its
+    definition: 1 sign bit, 5 exponent bits with bias 15, 2 mantissa bits,
+    subnormals m * 2^-16, S.11111.00 is infinity, S.11111.{01,10,11} NaN,
+    largest finite value 57344.  Same block rule with 57344 in place of 448
+    (fmt="e5m2").  P, where the simulation rounds it, stays E4M3.
 """
 from __future__ import annotations
 
@@ -75,6 +80,51 @@ def e4m3_encode(x):
     return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
+E5M2_MAX = 57344.0
+E5M2_BIAS = 15
+
+
+def e5m2_decode(codes):
+    """Decode uint8 OCP E5M2 codes to fp64 (+-inf for S.11111.00, NaN for
+    the other three codes of exponent 31)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    sub = m.astype(np.float64) * 2.0 ** (1 - E5M2_BIAS - 2)          # m/4 * 2^-14
+    nrm = (1.0 + m / 4.0) * np.exp2((e - E5M2_BIAS).astype(np.float64))
+    val = np.where(e == 0, sub, nrm)
+    val = np.where((e == 0x1F) & (m == 0), np.inf, val)
+    val = np.where((e == 0x1F) & (m != 0), np.nan, val)
+    return sign * val
+
+
+_POS_VALUES_E5M2 = e5m2_decode(np.arange(0x7C, dtype=np.uint8))   # finite: 0x00 .. 0x7B
+
+
+def e5m2_encode(x):
+    """Round fp64 values to the nearest finite E5M2 value, ties to the even
+    code, saturating at +-57344 (the block rule never exceeds it).  NaN maps
+    to 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.minimum(np.abs(x), E5M2_MAX)
+    hi = np.searchsorted(_POS_VALUES_E5M2, ax, side="left")
+    hi = np.minimum(hi, len(_POS_VALUES_E5M2) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = ax - _POS_VALUES_E5M2[lo]
+    d_hi = _POS_VALUES_E5M2[hi] - ax
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(ax == _POS_VALUES_E5M2[hi], hi, code)
+    code = code.astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+# format name -> (encode, decode, largest finite value)
+FORMATS = {"e4m3": (e4m3_encode, e4m3_decode, E4M3_MAX), "e5m2": (e5m2_encode, e5m2_decode, E5M2_MAX)}
+
+
 def sylvester_hadamard(d):
     """Dense unnormalised Sylvester Hadamard matrix, H_{2n} = [[H, H], [H, -H]]."""
     if d < 1 or d & (d - 1):
@@ -96,12 +146,14 @@ def rotate(x, signs):
     return (dx @ h.T) / np.sqrt(d)
 
 
-def block_quantize(x, block_rows=128):
-    """Per-(..., row block) E4M3 quantisation of x[..., N, d].
+def block_quantize(x, block_rows=128, fmt="e4m3"):
+    """Per-(..., row block) FP8 quantisation of x[..., N, d] (E4M3, or E5M2
+    with 57344 in place of 448).
 
     Returns (codes uint8 [..., N, d], scales fp64 [..., ceil(N/block_rows)],
     y fp64 [..., N, d]) where y = x * 448 / amax is the value each code
     rounds (kept so that tests can locate rounding boundaries)."""
+    encode, _, qmax = FORMATS[fmt]
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-2]
     nb = -(-n // block_rows)
@@ -118,36 +170,36 @@ def block_quantize(x, block_rows=128):
         # input of at most 50 significant bits and the division is correctly
         # rounded, so a value that lies exactly on a rounding midpoint stays
         # there and is decided by the ties-to-even rule
-        yb = np.where((amax > 0)[..., None, None], (blk * E4M3_MAX) / safe[..., None, None], 0.0)
+        yb = np.where((amax > 0)[..., None, None], (blk * qmax) / safe[..., None, None], 0.0)
         y[..., r0:r1, :] = yb
-        codes[..., r0:r1, :] = e4m3_encode(yb)
-        scales[..., b] = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        codes[..., r0:r1, :] = encode(yb)
+        scales[..., b] = np.where(amax > 0, amax / qmax, 1.0)
     return codes, scales, y
 
 
-def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False):
+def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, fmt="e4m3"):
     """The FP8 pre-pass: optional incoherent processing (signs given), then
-    per-block E4M3 quantisation.  Returns (codes, scales, y) with codes in
+    per-block quantisation to `fmt`.  Returns (codes, scales, y) with codes in
     [..., N, d] or, if transpose_out, [..., d, N] order."""
     xr = rotate(x, signs) if signs is not None else np.asarray(x, dtype=np.float64)
-    codes, scales, y = block_quantize(xr, block_rows)
+    codes, scales, y = block_quantize(xr, block_rows, fmt)
     if transpose_out:
         codes = np.swapaxes(codes, -1, -2).copy()
         y = np.swapaxes(y, -1, -2).copy()
     return codes, scales, y
 
 
-def dequantize(codes, scales, block_rows=128, transposed=False):
+def dequantize(codes, scales, block_rows=128, transposed=False, fmt="e4m3"):
     """x^ = decode(code) * scale of its row block."""
     c = np.swapaxes(codes, -1, -2) if transposed else codes
-    val = e4m3_decode(c)
+    val = FORMATS[fmt][1](c)
     n = val.shape[-2]
     row_scale = np.repeat(scales, block_rows, axis=-1)[..., :n]
     return val * row_scale[..., :, None]
 
 
 def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
-                            quantize_p=False, p_gain=256.0):
+                            quantize_p=False, p_gain=256.0, fmt="e4m3"):
     """Step-by-step simulation of FP8 attention (diagnostic floor).
 
     1. Rotate Q and K with the shared signs (skipped if signs is None).
@@ -159,9 +211,9 @@ def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
        pages leave the precision of P's second product open).
     Returns fp64 (O, LSE).
     """
-    qh = dequantize(*hadamard_rotate_quant(q, signs, block_rows)[:2], block_rows)
-    kh = dequantize(*hadamard_rotate_quant(k, signs, block_rows)[:2], block_rows)
-    vh = dequantize(*hadamard_rotate_quant(v, None, block_rows)[:2], block_rows)
+    qh = dequantize(*hadamard_rotate_quant(q, signs, block_rows, fmt=fmt)[:2], block_rows, fmt=fmt)
+    kh = dequantize(*hadamard_rotate_quant(k, signs, block_rows, fmt=fmt)[:2], block_rows, fmt=fmt)
+    vh = dequantize(*hadamard_rotate_quant(v, None, block_rows, fmt=fmt)[:2], block_rows, fmt=fmt)
     if not quantize_p:
         return _attention_exact(qh, kh, vh, scale, causal)
     lead = qh.shape[:-2]

@@ -51,6 +51,68 @@ def test_encode_round_trip_on_representable_values():
     np.testing.assert_array_equal(e4m3_encode(vals), codes)
 
 
+# ---------------------------------------------------------------- E5M2 codec
+# Closed-form values of the OCP E5M2 encoding (1.5.2, bias 15).
+KNOWN_E5M2 = {
+    0x00: 0.0, 0x01: 2.0 ** -16, 0x02: 2.0 ** -15, 0x03: 3 * 2.0 ** -16, 0x04: 2.0 ** -14,
+    0x3C: 1.0, 0x3D: 1.25, 0x3E: 1.5, 0x3F: 1.75, 0x40: 2.0, 0x78: 32768.0, 0x7B: 57344.0,
+    0x7C: math.inf, 0x80: -0.0, 0xBC: -1.0, 0xFB: -57344.0, 0xFC: -math.inf,
+}
+
+
+def test_e5m2_decode_known_values():
+    for code, val in KNOWN_E5M2.items():
+        got = float(oracle.e5m2_decode(np.uint8(code)))
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(code)
+    for code in (0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF):
+        assert np.isnan(oracle.e5m2_decode(np.uint8(code)))
+
+
+def test_e5m2_decode_exhaustive_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e5m2_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+
+
+def test_e5m2_encode_round_trip_ties_and_saturation():
+    pos = oracle.e5m2_decode(np.arange(0x7C, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0) and pos.max() == 57344.0
+    finite = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], np.uint8)
+    np.testing.assert_array_equal(oracle.e5m2_encode(oracle.e5m2_decode(finite)), finite)
+    cases = {1.125: 0x3C, 1.375: 0x3E, 1.625: 0x3E, 1.875: 0x40, 2.0 ** -17: 0x00,
+             3 * 2.0 ** -17: 0x02, 60000.0: 0x7B, 1e9: 0x7B, -1e9: 0xFB, -1.125: 0xBC}
+    for x, code in cases.items():
+        assert int(oracle.e5m2_encode(np.float64(x))) == code, x
+    assert int(oracle.e5m2_encode(np.float64(np.nan))) == 0x7F
+
+
+def test_e5m2_encode_matches_torch_after_clamp():
+    x = np.random.default_rng(5).standard_normal(20000) * np.exp2(np.random.default_rng(6).uniform(-20, 17, 20000))
+    xc = np.clip(x, -57344.0, 57344.0)
+    ref = torch.from_numpy(xc).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e5m2_encode(xc), ref)
+
+
+def test_e5m2_block_max_encodes_to_57344():
+    x = np.random.default_rng(7).standard_normal((2, 300, 64)) * 3
+    codes, scales, _ = block_quantize(x, 128, fmt="e5m2")
+    for b in range(3):
+        blk = codes[:, 128 * b:128 * (b + 1)]
+        xb = x[:, 128 * b:128 * (b + 1)]
+        amax = np.abs(xb).max(axis=(-2, -1))
+        np.testing.assert_allclose(scales[:, b], amax / 57344.0, rtol=0, atol=0)
+        for h in range(2):
+            i = np.unravel_index(np.argmax(np.abs(xb[h])), xb[h].shape)
+            assert blk[h][i] in (0x7B, 0xFB)
+    back = dequantize(codes, scales, 128, fmt="e5m2")
+    # 2 mantissa bits: relative error at most 2^-3 for normal values
+    big = np.abs(x) > np.abs(x).max() * 2.0 ** -14
+    assert np.all(np.abs(back - x)[big] <= np.abs(x)[big] * 2.0 ** -3 + 1e-12)
+
+
 def test_encode_ties_to_even_and_saturation():
     cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02,
              1.9375: 0x40, 15 * 2.0 ** -10: 0x08, 460.0: 0x7E, 1e6: 0x7E, -1e6: 0xFE,
