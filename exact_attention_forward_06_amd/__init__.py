@@ -16,14 +16,15 @@ from ._lib import (AttnError, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_mer
                    load, splitkv_chunk)
 
 
-def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=None):
+def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=None, fp8_format="e4m3"):
     """The whole FP8 path: rotate+quantise Q and K with the shared signs,
-    quantise V into the transposed layout, then the FP8 attention kernel."""
-    q8, sq = hadamard_rotate_quant(q, signs, stream=stream)
-    k8, sk = hadamard_rotate_quant(k, signs, stream=stream)
-    v8t, sv = hadamard_rotate_quant(v, None, transpose_out=True, stream=stream)
+    quantise V into the transposed layout, then the FP8 attention kernel
+    (codes in fp8_format: "e4m3" or "e5m2")."""
+    q8, sq = hadamard_rotate_quant(q, signs, stream=stream, fp8_format=fp8_format)
+    k8, sk = hadamard_rotate_quant(k, signs, stream=stream, fp8_format=fp8_format)
+    v8t, sv = hadamard_rotate_quant(v, None, transpose_out=True, stream=stream, fp8_format=fp8_format)
     return attn_fwd_fp8(q8, sq, k8, sk, v8t, sv, causal=causal, softmax_scale=softmax_scale,
-                        stream=stream)
+                        stream=stream, fp8_format=fp8_format)
 
 
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",

@@ -17,6 +17,7 @@ HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 _DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 
 _c_i64_3 = ctypes.c_int64 * 3
@@ -28,8 +29,8 @@ _SIGNATURES = {
     "attn_status_string": ([_i], ctypes.c_char_p),
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_fwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i, _vp], _i),
-    "hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp], _i),
-    "attn_fwd_fp8": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, ctypes.c_float,
+    "hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
+    "attn_fwd_fp8": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, ctypes.c_float,
                       _i, _vp], _i),
     "attn_fwd_splitkv": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                           ctypes.c_float, _i, _vp], _i),
@@ -163,9 +164,10 @@ def attn_merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None, s
 
 
 def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, out=None,
-                          scales=None, stream=None):
+                          scales=None, stream=None, fp8_format="e4m3"):
     """FP8 pre-pass of one [B, H, N, d] tensor: optional rotation by
-    (1/sqrt(d)) H diag(signs), per-block amax scale and E4M3 codes.
+    (1/sqrt(d)) H diag(signs), per-block amax scale and codes in fp8_format
+    ("e4m3" or "e5m2").
     Returns (codes uint8 [B,H,N,d] or [B,H,d,N], scales fp32 [B,H,nblk])."""
     lib = load()
     if x.dtype not in _DTYPE_CODE:
@@ -181,13 +183,13 @@ def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, ou
     if signs is not None and signs.dtype != torch.int8:
         raise ValueError("signs must be int8")
     _check(lib.hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides,
-                                     _ptr(signs), block_rows, int(bool(transpose_out)),
-                                     _ptr(out), _ptr(scales), _stream(stream)))
+                                     _ptr(signs), block_rows, FP8_FORMATS[fp8_format],
+                                     int(bool(transpose_out)), _ptr(out), _ptr(scales), _stream(stream)))
     return out, scales
 
 
 def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False, softmax_scale=None,
-                 block_rows=128, out=None, lse=None, return_lse=True, stream=None):
+                 block_rows=128, out=None, lse=None, return_lse=True, stream=None, fp8_format="e4m3"):
     """Attention forward on E4M3 codes (q8, k8 [B,H,N,d]; v8t [B,H,d,N]) with
     per-block fp32 scales.  Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
     lib = load()
@@ -201,8 +203,8 @@ def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False, softmax_s
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd_fp8(B, H, N, d, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
-                            _ptr(v8t), _ptr(v_scale), block_rows, _ptr(out), _ptr(lse), scale,
-                            int(bool(causal)), _stream(stream)))
+                            _ptr(v8t), _ptr(v_scale), block_rows, FP8_FORMATS[fp8_format], _ptr(out),
+                            _ptr(lse), scale, int(bool(causal)), _stream(stream)))
     return out, lse
 
 

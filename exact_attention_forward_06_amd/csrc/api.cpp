@@ -295,11 +295,14 @@ int attn_merge(int out_dtype, int S, int B, int H, int N, int d, const float* o_
 
 int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,
                           const int64_t* x_strides, const int8_t* signs, int block_rows,
-                          int transpose_out, uint8_t* x8, float* scales, void* stream) {
+                          int fp8_format, int transpose_out, uint8_t* x8, float* scales,
+                          void* stream) {
   const int es = elem_size(in_dtype);
   if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", in_dtype);
   if (int st = check_sizes(B, H, N, d)) return st;
   if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
+  if (fp8_format != ATTN_FP8_E4M3 && fp8_format != ATTN_FP8_E5M2)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown fp8_format %d", fp8_format);
   if (transpose_out != 0 && transpose_out != 1)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "transpose_out must be 0 or 1");
   if (transpose_out && N % 16 != 0)
@@ -329,6 +332,7 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* 
   a.sn = sn;
   a.signs = signs;
   a.block_rows = block_rows;
+  a.fp8_format = fp8_format;
   a.transpose_out = transpose_out != 0;
   a.x8 = x8;
   a.scales = scales;
@@ -340,11 +344,13 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* 
 
 int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_scale,
                  const uint8_t* k8, const float* k_scale, const uint8_t* v8t, const float* v_scale,
-                 int block_rows, void* o, float* lse, float softmax_scale, int causal,
-                 void* stream) {
+                 int block_rows, int fp8_format, void* o, float* lse, float softmax_scale,
+                 int causal, void* stream) {
   if (int st = check_sizes(B, H, N, d)) return st;
   if (int st = check_scale_causal(softmax_scale, causal)) return st;
   if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
+  if (fp8_format != ATTN_FP8_E4M3 && fp8_format != ATTN_FP8_E5M2)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown fp8_format %d", fp8_format);
   if (N % block_rows != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8 needs N a multiple of block_rows");
   if ((int64_t)N * d >= ((int64_t)1 << 31))
@@ -381,6 +387,7 @@ int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_s
   a.v8t = v8t;
   a.v_scale = v_scale;
   a.block_rows = block_rows;
+  a.fp8_format = fp8_format;
   a.o = o;
   a.lse = lse;
   a.scale = softmax_scale;

@@ -1,4 +1,5 @@
-// FP8 (OCP E4M3) attention forward for gfx950 with per-block scales.
+// FP8 (OCP E4M3, or E5M2 for Q, K and V) attention forward for gfx950 with
+// per-block scales.
 //
 // Inputs are the codes and block scales written by hadamard_rotate_quant:
 // Q8, K8 [B,H,N,d] (rotated by the same H D), V8t [B,H,d,N] (not rotated),
@@ -66,9 +67,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // becomes bit 4 of the key, so group g holds keys 16g .. 16g+15.
 __device__ __forceinline__ int key_of_row8(int r) { return (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3); }
 
+// FA, FB: operand formats of A and B (0: FP8 E4M3, 1: BF8 E5M2); no block
+// scale operands.
+template <int FA, int FB>
 __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
-  // cbsz = blgp = 0: both operands FP8 E4M3; no block scale.
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ i32x8_t cat(u32x4_t lo, u32x4_t hi) {
@@ -107,7 +110,8 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, char* dst, int wa
                                              0, 0);
 }
 
-template <int D, int BN, bool CAUSAL>
+// FMT: format of the Q, K and V codes (0: E4M3, 1: E5M2); P is always E4M3.
+template <int D, int BN, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_kernel(F8Params p) {
   constexpr int NT = 256, BLOCK_M = 128;
@@ -222,7 +226,7 @@ void attn_fwd_fp8_kernel(F8Params p) {
       for (int ks = 0; ks < NKS; ++ks) {
         const i32x8_t a = cat(*(const lds_u32x4_t*)(sb + kb * 32 * KRB + kaddr[ks][0]),
                               *(const lds_u32x4_t*)(sb + kb * 32 * KRB + kaddr[ks][1]));
-        sacc[kb] = mfma_fp8(a, qf[ks], sacc[kb]);
+        sacc[kb] = mfma_fp8<FMT, FMT>(a, qf[ks], sacc[kb]);
       }
     }
 
@@ -286,7 +290,7 @@ void attn_fwd_fp8_kernel(F8Params p) {
       for (int t = 0; t < NPV; ++t) {
         const i32x8_t a = cat(*(const lds_u32x4_t*)(sb + db * 32 * VRB + vaddr[t][0]),
                               *(const lds_u32x4_t*)(sb + db * 32 * VRB + vaddr[t][1]));
-        oacc[db] = mfma_fp8(a, pf[t], oacc[db]);
+        oacc[db] = mfma_fp8<FMT, 0>(a, pf[t], oacc[db]);
       }
   };
 
@@ -353,7 +357,7 @@ __device__ __forceinline__ void phase_barrier8() {
 template <int V>
 using ic8 = std::integral_constant<int, V>;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_pp_kernel(F8Params p) {
   constexpr int BN = 128, NT = 512, NTC = 256, BLOCK_M = 256;
@@ -503,17 +507,17 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
 #pragma unroll
     for (int i = 0; i < NOPS; ++i) {
       if (i + LA < NOPS) load(i + LA);
-      sacc[i % NKB] = mfma_fp8(kf[i], qf[i / NKB], sacc[i % NKB]);
-      oacc[i % NDB] = mfma_fp8(vf[i], pf[i / NDB], oacc[i % NDB]);
+      sacc[i % NKB] = mfma_fp8<FMT, FMT>(kf[i], qf[i / NKB], sacc[i % NKB]);
+      oacc[i % NDB] = mfma_fp8<FMT, 0>(vf[i], pf[i / NDB], oacc[i % NDB]);
       __builtin_amdgcn_sched_barrier(0);
     }
     {
       f32x16_t z;
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = 0.f;
-      lacc = mfma_fp8(ones, pf[0], z);
+      lacc = mfma_fp8<0, 0>(ones, pf[0], z);
 #pragma unroll
-      for (int t = 1; t < NPV; ++t) lacc = mfma_fp8(ones, pf[t], lacc);
+      for (int t = 1; t < NPV; ++t) lacc = mfma_fp8<0, 0>(ones, pf[t], lacc);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -652,7 +656,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 hipError_t launch_pp(const Fp8FwdArgs& a, hipStream_t s) {
   constexpr int BLOCK_M = 256;
   F8Params p;
@@ -670,11 +674,11 @@ hipError_t launch_pp(const Fp8FwdArgs& a, hipStream_t s) {
   p.total = a.B * a.H * p.nmb;
   p.nblk = a.N / a.block_rows;
   p.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_fp8_pp_kernel<D, CAUSAL>), dim3(p.total), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_fp8_pp_kernel<D, CAUSAL, FMT>), dim3(p.total), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, int FMT>
 hipError_t launch_one(const Fp8FwdArgs& a, hipStream_t s) {
   constexpr int BLOCK_M = 128;
   F8Params p;
@@ -692,13 +696,24 @@ hipError_t launch_one(const Fp8FwdArgs& a, hipStream_t s) {
   p.total = a.B * a.H * p.nmb;
   p.nblk = a.N / a.block_rows;
   p.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, BN, CAUSAL>), dim3(p.total), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, BN, CAUSAL, FMT>), dim3(p.total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <int D, int BN>
+template <int D, int BN, int FMT>
 hipError_t launch_mask(const Fp8FwdArgs& a, hipStream_t s) {
-  return a.causal ? launch_one<D, BN, true>(a, s) : launch_one<D, BN, false>(a, s);
+  return a.causal ? launch_one<D, BN, true, FMT>(a, s) : launch_one<D, BN, false, FMT>(a, s);
+}
+
+template <int FMT>
+hipError_t launch_fmt(const Fp8FwdArgs& a, hipStream_t stream, bool* supported) {
+  switch (a.d) {
+    case 64: return a.causal ? launch_pp<64, true, FMT>(a, stream) : launch_pp<64, false, FMT>(a, stream);
+    case 128: return a.causal ? launch_pp<128, true, FMT>(a, stream) : launch_pp<128, false, FMT>(a, stream);
+    case 256: return launch_mask<256, 64, FMT>(a, stream);
+  }
+  *supported = false;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -709,10 +724,9 @@ hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* su
     *supported = false;
     return hipSuccess;
   }
-  switch (a.d) {
-    case 64: return a.causal ? launch_pp<64, true>(a, stream) : launch_pp<64, false>(a, stream);
-    case 128: return a.causal ? launch_pp<128, true>(a, stream) : launch_pp<128, false>(a, stream);
-    case 256: return launch_mask<256, 64>(a, stream);
+  switch (a.fp8_format) {
+    case 0: return launch_fmt<0>(a, stream, supported);
+    case 1: return launch_fmt<1>(a, stream, supported);
   }
   *supported = false;
   return hipSuccess;

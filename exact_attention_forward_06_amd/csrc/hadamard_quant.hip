@@ -1,4 +1,5 @@
-// FP8 pre-pass for gfx950: incoherent processing + per-block E4M3 codes.
+// FP8 pre-pass for gfx950: incoherent processing + per-block E4M3 (or E5M2)
+// codes.
 //
 // For each row x of one (b, h): x~ = H D x over the head dimension (D the
 // random +-1 diagonal, H the Sylvester Hadamard matrix), then per block of
@@ -23,6 +24,10 @@
 //    on gfx950) after clamping to +-448; the value rounded is the quotient
 //    (x~ * 448) / amax with an FMA remainder correction, not x~ times a
 //    rounded 448 / amax, so exact rounding ties stay exact.
+//  * E5M2 (FMT = 1, the other FP8 format of the "FlashAttention-2/3" page,
+//    特性二): the same rule with 57344 (its largest finite value) in place of
+//    448, codes from v_cvt_pk_bf8_f32 (OCP E5M2 on gfx950).  448 and 57344
+//    share the significand 1.75, so the quotient stays exact alike.
 //  * transpose_out writes [d][n] (the layout the FP8 attention kernel wants
 //    for V): codes are transposed through LDS so global stores stay 16-byte.
 #include "kernels.h"
@@ -72,8 +77,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-template <typename T, int D, bool ROT, bool TRANS>
+template <typename T, int D, bool ROT, bool TRANS, int FMT>
 __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
+  constexpr float QMAX = FMT == 0 ? 448.f : 57344.f;   // largest finite E4M3 / E5M2 value
   constexpr int EPL = D / LPR;                  // elements per lane
   constexpr int ES = sizeof(T);
   constexpr int LOADS = EPL * ES / 16;          // 16-byte loads per lane per row
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
   // so a quotient that is representable (e.g. an exact E4M3 rounding tie,
   // frequent for 16-bit inputs whose x * 448 is exact) comes out exactly.
   const float ramax = amax > 0.f ? 1.f / amax : 0.f;
-  if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax > 0.f ? amax * p.scale_norm / 448.f : 1.f;
+  if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax > 0.f ? amax * p.scale_norm / QMAX : 1.f;
 
   // codes
   uint8_t* out = p.x8 + (int64_t)bh * p.N * D;
@@ -170,13 +176,18 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
       float y[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float a = v[ps][4 * w + t] * 448.f;
+        const float a = v[ps][4 * w + t] * QMAX;
         const float y0 = a * ramax;
         const float q = fmaf(fmaf(-y0, amax, a), ramax, y0);
-        y[t] = fminf(fmaxf(q, -448.f), 448.f);
+        y[t] = fminf(fmaxf(q, -QMAX), QMAX);
       }
-      unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      words[w] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      if constexpr (FMT == 0) {
+        unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        words[w] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      } else {
+        unsigned lo = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+        words[w] = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], lo, true);
+      }
     }
     if constexpr (!TRANS) {
       if (row < p.N) {
@@ -207,8 +218,8 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
   }
 }
 
-template <typename T, int D>
-hipError_t launch_d(const QuantArgs& a, hipStream_t s) {
+template <typename T, int D, int FMT>
+hipError_t launch_f(const QuantArgs& a, hipStream_t s) {
   QParams p;
   p.x = static_cast<const char*>(a.x);
   p.sb = a.sb;
@@ -223,13 +234,18 @@ hipError_t launch_d(const QuantArgs& a, hipStream_t s) {
   p.scale_norm = a.signs ? 1.f / sqrtf((float)D) : 1.f;
   dim3 grid(p.nblk, a.B * a.H);
   if (a.signs) {
-    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false>), grid, dim3(NT), 0, s, p);
+    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, true, FMT>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false, FMT>), grid, dim3(NT), 0, s, p);
   } else {
-    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false>), grid, dim3(NT), 0, s, p);
+    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, true, FMT>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false, FMT>), grid, dim3(NT), 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const QuantArgs& a, hipStream_t s) {
+  return a.fp8_format == 0 ? launch_f<T, D, 0>(a, s) : launch_f<T, D, 1>(a, s);
 }
 
 template <typename T>
@@ -247,7 +263,7 @@ hipError_t launch_t(const QuantArgs& a, hipStream_t s, bool* ok) {
 }  // namespace
 
 hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported) {
-  if (a.block_rows != ROWS) {
+  if (a.block_rows != ROWS || (a.fp8_format != 0 && a.fp8_format != 1)) {
     *supported = false;
     return hipSuccess;
   }

@@ -42,6 +42,7 @@ struct QuantArgs {
   int64_t sb, sh, sn;
   const int8_t* signs;  // nullptr = no rotation
   int block_rows;
+  int fp8_format;       // 0: E4M3, 1: E5M2
   bool transpose_out;
   uint8_t* x8;
   float* scales;
@@ -56,6 +57,7 @@ struct Fp8FwdArgs {
   const uint8_t* v8t;
   const float* v_scale;
   int block_rows;
+  int fp8_format;       // codes of q8, k8, v8t: 0 E4M3, 1 E5M2
   void* o;              // bf16 [B, H, N, d]
   float* lse;
   float scale;

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum {
@@ -62,6 +62,11 @@ enum {
 
 /* Element types of Q, K, V and O. */
 enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
+
+/* FP8 code formats (OCP): E4M3 (largest finite 448, no infinities) and E5M2
+ * (largest finite 57344) -- the two FP8 formats the "FlashAttention-2/3" page
+ * names (FlashAttention-3 特性二). */
+enum { ATTN_FP8_E4M3 = 0, ATTN_FP8_E5M2 = 1 };
 
 /* ABI version of the loaded library (ATTN_ABI_VERSION it was built with). */
 int attn_abi_version(void);
@@ -175,9 +180,10 @@ int attn_merge(int out_dtype, int S, int B, int H, int N, int d,
  * with D = diag(signs) and H the Sylvester-order Hadamard matrix
  * (H[i][j] = (-1)^popcount(i & j)); otherwise x~ = x.  Then, per
  * (b, h, block of block_rows consecutive rows) over all d columns:
- * amax = max |x~|, scale = amax / 448 (1 if amax = 0), and
- * code = E4M3FN round-to-nearest-even of x~ * 448 / amax (OCP FP8 E4M3,
- * bias 7, max 448).  Dequantisation is x~ = decode(code) * scale.
+ * amax = max |x~|, scale = amax / Q (1 if amax = 0), and
+ * code = round-to-nearest-even of x~ * Q / amax in the chosen format, with
+ * Q = 448 for OCP E4M3 (bias 7) and Q = 57344 for OCP E5M2 (bias 15).
+ * Dequantisation is x~ = decode(code) * scale.
  *
  *   in_dtype       ATTN_F32, ATTN_F16 or ATTN_BF16 (type of x).
  *   B, H, N, d     shape of x; d in {64, 128, 256}.
@@ -185,6 +191,7 @@ int attn_merge(int out_dtype, int S, int B, int H, int N, int d,
  *   signs          device int8 [d] of +-1 (shared by the Q and K calls), or
  *                  NULL for no rotation (V, and the unrotated comparison).
  *   block_rows     rows per scale block; must be 128.
+ *   fp8_format     ATTN_FP8_E4M3 or ATTN_FP8_E5M2.
  *   transpose_out  0: x8 is [B, H, N, d];  1: x8 is [B, H, d, N] (the layout
  *                  attn_fwd_fp8 wants for V).
  *   x8             device uint8 output codes.
@@ -193,11 +200,12 @@ int attn_merge(int out_dtype, int S, int B, int H, int N, int d,
  */
 int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
                           const void* x, const int64_t* x_strides,
-                          const int8_t* signs, int block_rows, int transpose_out,
-                          uint8_t* x8, float* scales, void* stream);
+                          const int8_t* signs, int block_rows, int fp8_format,
+                          int transpose_out, uint8_t* x8, float* scales,
+                          void* stream);
 
 /*
- * attn_fwd_fp8 -- attention forward on FP8 E4M3 codes with per-block scales.
+ * attn_fwd_fp8 -- attention forward on FP8 codes with per-block scales.
  *
  *   q8, k8         device uint8 [B, H, N, d] codes (hadamard_rotate_quant
  *                  with the same signs for both), q_scale / k_scale device
@@ -205,13 +213,16 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  *   v8t            device uint8 [B, H, d, N] codes (transpose_out = 1, no
  *                  rotation), v_scale device fp32 [B, H, N/block_rows].
  *   block_rows     128; N must be a multiple of block_rows.
+ *   fp8_format     format of q8, k8 and v8t: ATTN_FP8_E4M3 or ATTN_FP8_E5M2
+ *                  (all three the same; the MFMA reads either natively).
  *   o              device bf16 output [B, H, N, d].
  *   lse            device fp32 [B, H, N] or NULL.
  *   softmax_scale, causal, stream as in attn_fwd.
  *
  * Both products run on FP8 MFMA with fp32 accumulation: S = Q8 K8^T with
  * the two block scales and softmax_scale folded into one factor per tile,
- * and O += P V where P is rounded to E4M3 after multiplication by a gain
+ * and O += P V where P is rounded to E4M3 (whatever fp8_format is) after
+ * multiplication by a gain
  * of 16 * sV_j / max_j sV_j (sV_j the scale of V's key block j), so that
  * the V block scales fold into P and the lazy rescale threshold of 2^4
  * keeps the scaled P at most 256.  The row sums l are those of the rounded
@@ -225,7 +236,7 @@ int attn_fwd_fp8(int B, int H, int N, int d,
                  const uint8_t* q8, const float* q_scale,
                  const uint8_t* k8, const float* k_scale,
                  const uint8_t* v8t, const float* v_scale,
-                 int block_rows,
+                 int block_rows, int fp8_format,
                  void* o, float* lse,
                  float softmax_scale, int causal, void* stream);
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
                           "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -85,9 +85,9 @@ def test_attn_fwd_rejects(lib, kw, status, msg):
 
 
 def _quant(lib, dtype=2, B=1, H=1, N=256, d=128, x=A, strides=None, signs=B_, block_rows=128,
-           t=0, x8=O, sc=L):
+           fmt=0, t=0, x8=O, sc=L):
     s = None if strides is None else (ctypes.c_int64 * 3)(*strides)
-    return lib.hadamard_rotate_quant(dtype, B, H, N, d, x, s, signs, block_rows, t, x8, sc, None)
+    return lib.hadamard_rotate_quant(dtype, B, H, N, d, x, s, signs, block_rows, fmt, t, x8, sc, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -100,6 +100,8 @@ def _quant(lib, dtype=2, B=1, H=1, N=256, d=128, x=A, strides=None, signs=B_, bl
     (dict(N=100, t=1), 2, "multiple of 16"),
     (dict(x8=A), 1, "overlap"),
     (dict(dtype=-1), 1, "unknown dtype"),
+    (dict(fmt=2), 1, "fp8_format"),
+    (dict(fmt=-1), 1, "fp8_format"),
 ])
 def test_quant_rejects(lib, kw, status, msg):
     assert _quant(lib, **kw) == status
@@ -107,8 +109,8 @@ def test_quant_rejects(lib, kw, status, msg):
 
 
 def _fp8(lib, B=1, H=1, N=256, d=128, q8=A, qs=A + 0x8000000, k8=B_, ks=B_ + 0x8000000, v8=C,
-         vs=C + 0x8000000, block_rows=128, o=O, lse=L, scale=0.088, causal=0):
-    return lib.attn_fwd_fp8(B, H, N, d, q8, qs, k8, ks, v8, vs, block_rows, o, lse, scale, causal,
+         vs=C + 0x8000000, block_rows=128, fmt=0, o=O, lse=L, scale=0.088, causal=0):
+    return lib.attn_fwd_fp8(B, H, N, d, q8, qs, k8, ks, v8, vs, block_rows, fmt, o, lse, scale, causal,
                             None)
 
 
@@ -120,6 +122,7 @@ def _fp8(lib, B=1, H=1, N=256, d=128, q8=A, qs=A + 0x8000000, k8=B_, ks=B_ + 0x8
     (dict(d=48), 2, "head dimension"),
     (dict(o=B_), 1, "overlaps"),
     (dict(causal=-1), 1, "causal"),
+    (dict(fmt=3), 1, "fp8_format"),
 ])
 def test_fp8_rejects(lib, kw, status, msg):
     assert _fp8(lib, **kw) == status
