@@ -156,6 +156,48 @@ def merge_partials(o_parts, lse_parts):
     return o, lse
 
 
+def attention_backward_head(q, k, v, do, scale, causal=False):
+    """Gradients of one head's attention output O = softmax(S) V, S = Q K^T *
+    scale (masked entries -inf), with respect to Q, K and V for an upstream
+    gradient dO: the chain rule through the three unfused steps, with S and P
+    materialised.  The pages name the backward pass ("FlashAttention-3" page,
+    section "适用范围和工程限制": fp16/bf16 forward and backward) and its
+    recomputation of P from the stored logsumexp ("Flash Attention V3" page,
+    sections 2.1 and 2.2) without a formula; this is the plain gradient:
+
+        dV = P^T dO
+        dP = dO V^T
+        dS_ij = P_ij (dP_ij - D_i),   D_i = sum_j P_ij dP_ij = dO_i . O_i
+        dQ = dS K * scale,   dK = dS^T Q * scale
+
+    Returns fp64 (dQ, dK, dV).
+    """
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    s = scores(q, k, scale, causal)
+    p, _, _ = row_softmax(s)
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = np.sum(p * dp, axis=1)
+    ds = p * (dp - dsum[:, None])
+    dq = ds @ k * float(scale)
+    dk = ds.T @ q * float(scale)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, scale, causal=False):
+    """Batched [..., N, d] version of attention_backward_head (one head at a
+    time).  Returns fp64 (dQ, dK, dV)."""
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    outs = [np.empty((int(np.prod(lead)) if lead else 1, n, d), np.float64) for _ in range(3)]
+    qf, kf, vf, df = (x.reshape(-1, n, d) for x in (q, k, v, do))
+    for h in range(qf.shape[0]):
+        for o, g in zip(outs, attention_backward_head(qf[h], kf[h], vf[h], df[h], scale, causal)):
+            o[h] = g
+    return tuple(o.reshape(*lead, n, d) for o in outs)
+
+
 def credited_flops(B, H, N, d, causal):
     """Throughput convention: 4*B*H*N^2*d, halved under the causal mask."""
     f = 4.0 * B * H * N * N * d

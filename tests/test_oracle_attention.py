@@ -328,3 +328,54 @@ def test_batched_layout():
 def test_credited_flops():
     assert oracle.credited_flops(2, 16, 8192, 128, True) == 549755813888.0
     assert oracle.credited_flops(4, 16, 2048, 128, False) == 137438953472.0
+
+
+# ------------------------------------------------------------------ backward
+def _loss(q, k, v, do, scale, causal):
+    return float(np.sum(attention_head(q, k, v, scale, causal)[0] * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(causal):
+    """Central differences of L = sum(dO * O) in a few random directions of
+    Q, K and V against the oracle's gradients (first-order identity)."""
+    n, d = 9, 5
+    q, k, v, do = (_rand((n, d), s) for s in (80, 81, 82, 83))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_backward_head(q, k, v, do, scale, causal)
+    rng = np.random.default_rng(84)
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(3):
+            e = rng.standard_normal((n, d))
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p = [a + eps * e if i == which else a for i, a in enumerate(args_p)]
+            args_m = [a - eps * e if i == which else a for i, a in enumerate(args_m)]
+            fd = (_loss(*args_p, do, scale, causal) - _loss(*args_m, do, scale, causal)) / (2 * eps)
+            assert abs(fd - float(np.sum(grad * e))) <= 1e-7 * max(1.0, abs(fd)), (which, fd)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd_fp64(causal):
+    n, d = 40, 16
+    q, k, v, do = (_rand((2, n, d), s) for s in (85, 86, 87, 88))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.25, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.25)
+    out.backward(torch.tensor(do))
+    for ours, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """Rows of dS sum to zero (so the key gradients sum to zero), and the
+    value gradients sum to the summed upstream gradient (rows of P sum to 1)."""
+    n, d = 30, 8
+    q, k, v, do = (_rand((n, d), s) for s in (89, 90, 91, 92))
+    dq, dk, dv = oracle.attention_backward_head(q, k, v, do, 0.5, causal)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+    if causal:   # query 0 sees only key 0: its dS row is P_00 (dP_00 - D_0) = 0
+        np.testing.assert_allclose(dq[0], 0.0, atol=1e-14)
