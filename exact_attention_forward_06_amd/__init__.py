@@ -11,8 +11,9 @@ Public API (thin wrappers over the C ABI of libattn.so, include/attn.h):
     attn_fwd_splitkv(q, k, v, num_splits, causal=False)
         -> (o, lse, o_part, lse_part)
     attn_merge(o_part, lse_part, out_dtype) -> (o, lse)
+    attn_bwd(q, k, v, o, lse, dout, causal=False) -> (dq, dk, dv, delta)
 """
-from ._lib import (AttnError, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_merge, hadamard_rotate_quant,
+from ._lib import (AttnError, attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_merge, hadamard_rotate_quant,
                    load, splitkv_chunk)
 
 
@@ -27,5 +28,5 @@ def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=No
                         stream=stream, fp8_format=fp8_format)
 
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
+__all__ = ["AttnError", "attn_bwd", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
            "hadamard_rotate_quant", "load", "splitkv_chunk"]

@@ -35,6 +35,8 @@ _SIGNATURES = {
     "attn_fwd_splitkv": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                           ctypes.c_float, _i, _vp], _i),
     "attn_merge": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
+    "attn_bwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                  _i, _vp], _i),
 }
 
 _lib = None
@@ -206,6 +208,40 @@ def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False, softmax_s
                             _ptr(v8t), _ptr(v_scale), block_rows, FP8_FORMATS[fp8_format], _ptr(out),
                             _ptr(lse), scale, int(bool(causal)), _stream(stream)))
     return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd for the upstream gradient dout,
+    from the forward's inputs and outputs (o, lse) -- fp16 / bf16, d = 64 or
+    128, contiguous [B, H, N, d] tensors.  `delta` (fp32 [B, H, N]) is the
+    library's workspace, allocated unless given; on return it holds
+    dO_i . O_i.  Returns (dq, dk, dv, delta)."""
+    lib = load()
+    if q.dtype not in _DTYPE_CODE or any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must share a dtype among fp16, bf16")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32")
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("attn_bwd takes contiguous tensors")
+    B, H, N, d = q.shape
+    for t in (k, v, o, dout):
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_bwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                        _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)),
+                        _stream(stream)))
+    return dq, dk, dv, delta
 
 
 def declared_symbols(header: str = HEADER_PATH):

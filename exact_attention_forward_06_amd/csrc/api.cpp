@@ -399,3 +399,63 @@ int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_s
 }
 
 }  // extern "C"
+
+extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const void* dout,
+                        float* delta, void* dq, void* dk, void* dv, float softmax_scale,
+                        int causal, void* stream) {
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (int st = check_scale_causal(softmax_scale, causal)) return st;
+  if (dtype == ATTN_F32 || d == 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd covers fp16 / bf16 with d = 64 or 128");
+  const int64_t rows = (int64_t)B * H * N;
+  const int64_t tbytes = rows * d * es;
+  Span sq, sk, sv, so, sl, sdo, sdl, sdq, sdk, sdv;
+  if (int st = check_dense("q", q, tbytes, &sq)) return st;
+  if (int st = check_dense("k", k, tbytes, &sk)) return st;
+  if (int st = check_dense("v", v, tbytes, &sv)) return st;
+  if (int st = check_dense("o", o, tbytes, &so)) return st;
+  if (int st = check_dense("lse", lse, rows * 4, &sl, false)) return st;
+  if (int st = check_dense("dout", dout, tbytes, &sdo)) return st;
+  if (int st = check_dense("delta", delta, rows * 4, &sdl, false)) return st;
+  if (int st = check_dense("dq", dq, tbytes, &sdq)) return st;
+  if (int st = check_dense("dk", dk, tbytes, &sdk)) return st;
+  if (int st = check_dense("dv", dv, tbytes, &sdv)) return st;
+  const Span ins[6] = {sq, sk, sv, so, sl, sdo};
+  const Span outs[4] = {sdl, sdq, sdk, sdv};
+  for (int i = 0; i < 4; ++i) {
+    for (const Span& in : ins)
+      if (overlaps(outs[i], in)) return fail(ATTN_ERR_INVALID_ARGUMENT, "an output overlaps an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs overlap each other");
+  }
+  // one head's rows are addressed with 32-bit buffer offsets (including up
+  // to one 64-row tile past N, which reads as zero)
+  if (((int64_t)N + 64) * d * es >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
+
+  attn::BwdArgs a;
+  a.dtype = static_cast<attn::Dtype>(dtype);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  bool supported = true;
+  hipError_t e = attn::launch_attn_bwd(a, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_bwd kernel for dtype %d d=%d", dtype, d);
+  return hip_status(e, "attn_bwd launch");
+}

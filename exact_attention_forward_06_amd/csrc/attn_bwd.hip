@@ -1,0 +1,537 @@
+// Exact-attention backward for gfx950, fp16 / bf16 inputs with d = 64 or 128:
+// dQ, dK, dV of O = softmax(Q K^T * scale) V for an upstream gradient dO,
+// with P recomputed tile by tile from the forward's stored logsumexp so that,
+// as in the forward, no N x N matrix reaches device memory.
+//
+// Method.  The pages name the backward pass ("FlashAttention-3" page, section
+// "适用范围和工程限制": fp16/bf16 forward and backward) and the role of the
+// stored LSE in it ("Flash Attention V3" page, sections 2.1 and 2.2: the
+// backward recomputes P from the saved softmax statistics instead of storing
+// P).  Per (b, h), with c = scale * log2(e) and D_i = dO_i . O_i:
+//     P_ij  = exp2(c s_ij - log2(e) LSE_i)          (0 where masked)
+//     dP_ij = dO_i . V_j
+//     dS_ij = P_ij (dP_ij - D_i)
+//     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K
+// (the chain rule through softmax; D_i = sum_j P_ij dP_ij = dO_i . O_i).
+//
+// Two launches, no atomics, deterministic:
+//  * attn_bwd_dq_kernel: one workgroup per (b, h, 128 query rows); streams
+//    K/V tiles like the forward.  Its prologue also computes D_i from O and
+//    dO and stores it in the caller's workspace for the second launch.
+//  * attn_bwd_dkdv_kernel: one workgroup per (b, h, 128 keys); streams Q/dO
+//    tiles (and their LSE / D values) and accumulates dK and dV.
+//
+// gfx950 mapping (the forward's operand layouts, attn16_common.h)
+//  * 4 wave64 per workgroup, 32 stationary rows per wave, held as the
+//    B operand of v_mfma_f32_32x32x16_{bf16,f16} in VGPRs (dq: Q and dO;
+//    dkdv: K and V).  The streamed 64-row tiles go global -> LDS with
+//    buffer_load ... lds, double-buffered, into the XOR-swizzled row layout.
+//  * dq kernel: S^T = K Q^T and dP^T = V dO^T (lane = one query, registers =
+//    16 of the tile's keys, key order permuted so registers 8c..8c+7 hold 8
+//    consecutive keys); dS^T rounded to 16 bits is directly the B operand of
+//    dQ^T += K^T dS^T, whose A operand is read transposed from the K tile
+//    with ds_read_b64_tr_b16.
+//  * dkdv kernel: the mirror image: S = Q K^T and dP = dO V^T with lane = one
+//    key; P and dS are the B operands of dV^T += dO^T P and dK^T += Q^T dS,
+//    with dO^T and Q^T read transposed from the streamed tiles.
+//  * Causal: the dq kernel never loads K/V tiles past its block's last
+//    query; the dkdv kernel starts at the first Q tile that can see its
+//    block's keys.  Element masks run only on tiles that straddle the
+//    diagonal or the end of the sequence.
+#include "attn16_common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace attn {
+namespace {
+
+struct BwdParams {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* o;
+  const char* dout;
+  const float* lse;
+  float* delta;          // fp32 [B, H, N]: written by the dq kernel, read by dkdv
+  char* dq;
+  char* dk;
+  char* dv;
+  int N, nblk, total;
+  float scale;           // softmax scale
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+constexpr int kBwdThreads = 256;   // 4 wave64
+constexpr int kBwdBlock = 128;     // stationary rows per workgroup (32 per wave)
+constexpr int kBwdTile = 64;       // streamed rows per LDS tile
+
+// Row addresses inside an LDS tile of the swizzled [row][D] layout.
+//  rows(ks): the A operand "row-major" read -- lane (n, g) reads the 16 bytes
+//    of logical chunk 2 ks + g of row key_of_row(n) (add kb * 32 * RB for the
+//    kb-th 32-row block).
+//  tr(db, half): the transposed read (ds_read_b64_tr_b16) -- lanes get one
+//    column d of 4 consecutive rows; add cc * 16 * RB for the cc-th 16-row
+//    chunk.
+template <int D>
+struct TileAddr {
+  static constexpr int RB = D * 2;
+  static constexpr int NKS = D / 16;
+  static constexpr int NDB = D / 32;
+  int rows[NKS];
+  int tr[NDB][2];
+  __device__ __forceinline__ explicit TileAddr(int lane) {
+    const int n = lane & 31, g = lane >> 5;
+    const int krow = key_of_row(n);
+    const int kswz = swz<D>(krow);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) rows[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
+    const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
+    const int vg = hq >> 1;
+    const int vcol0 = (hq & 1) * 16 + 4 * ta;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row = vg * 8 + half * 4 + te;
+        const int col = db * 32 + vcol0;
+        tr[db][half] = row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+      }
+  }
+};
+
+// Transposed A operand (16-row chunk starting at `base`, d block db).
+template <typename frag, int D>
+__device__ __forceinline__ frag read_tr(const char* base, const TileAddr<D>& ta, int db) {
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + ta.tr[db][0]));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + ta.tr[db][1]));
+  u32x4_t w;
+  w[0] = __builtin_bit_cast(u32x2_t, lo)[0];
+  w[1] = __builtin_bit_cast(u32x2_t, lo)[1];
+  w[2] = __builtin_bit_cast(u32x2_t, hi)[0];
+  w[3] = __builtin_bit_cast(u32x2_t, hi)[1];
+  return __builtin_bit_cast(frag, w);
+}
+
+// acc[kb] = X Y^T for 32-row block kb of an LDS tile X (rows read permuted)
+// against the resident B fragments yf (one stationary row per lane).
+template <typename T, int D, int NKB>
+__device__ __forceinline__ void tile_dot(f32x16_t (&acc)[NKB], const char* tile, const TileAddr<D>& ta,
+                                         const typename Ops<T>::frag (&yf)[D / 16]) {
+  using frag = typename Ops<T>::frag;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(tile + kb * 32 * TileAddr<D>::RB + ta.rows[ks]));
+      acc[kb] = Ops<T>::mfma(a, yf[ks], acc[kb]);
+    }
+  }
+}
+
+// Load one stationary row's B fragments: lane (n, g) holds
+// row[16 ks + 8 g .. + 8] (zeros past the end of the sequence).
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frags(typename Ops<T>::frag (&f)[D / 16], const char* row, bool valid, int g) {
+  using frag = typename Ops<T>::frag;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *(const u32x4_t*)(row + ks * 32 + g * 16);
+    f[ks] = __builtin_bit_cast(frag, raw);
+  }
+}
+
+// Store a [D x 32] transposed accumulator (lane = row n of the output, its
+// registers = d) times `mul` as 16-bit values of the row `dst`.
+template <typename T, int D>
+__device__ __forceinline__ void store_rowT(char* dst, const f32x16_t (&acc)[D / 32], float mul, int g) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int d0 = db * 32 + t * 8 + g * 4;
+      u32x2_t w = {Ops<T>::pack2(acc[db][4 * t] * mul, acc[db][4 * t + 1] * mul),
+                   Ops<T>::pack2(acc[db][4 * t + 2] * mul, acc[db][4 * t + 3] * mul)};
+      *(u32x2_t*)(dst + d0 * 2) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D_i).  Grid: (b, h, 128-query block), XCD-grouped per head; under
+// the causal mask the blocks with the most K/V tiles go first.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(BwdParams p) {
+  using Op = Ops<T>;
+  using frag = typename Op::frag;
+  constexpr int NT = kBwdThreads, BN = kBwdTile;
+  constexpr int RB = D * 2;
+  constexpr int TILE = BN * RB;
+  constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NCC = BN / 16;
+  constexpr int LOADS = TILE / (NT * 16);
+  static_assert(TILE % (NT * 16) == 0, "tile split");
+
+  __shared__ __attribute__((aligned(1024))) char sk0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sk1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sv1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int N = p.N;
+
+  const int logical = xcd_logical_id(blockIdx.x, p.total);
+  const int bh = logical / p.nblk;
+  int mb = logical - bh * p.nblk;
+  if (CAUSAL) mb = p.nblk - 1 - mb;
+  const int m0 = mb * kBwdBlock;
+  const int wq0 = m0 + wave * 32;
+  const int q_row = wq0 + n;
+  const bool q_ok = q_row < N;
+  const int64_t head = (int64_t)bh * N;      // row index of the head's first row
+  const int64_t row_off = (head + q_row) * RB;
+
+  frag qf[NKS], dof[NKS];
+  load_row_frags<T, D>(qf, p.q + row_off, q_ok, g);
+  load_row_frags<T, D>(dof, p.dout + row_off, q_ok, g);
+
+  // D_i = dO_i . O_i (fp32 products of the 16-bit values), stored for dkdv
+  float delta;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (q_ok) raw = *(const u32x4_t*)(p.o + row_off + ks * 32 + g * 16);
+      const frag of = __builtin_bit_cast(frag, raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)of[e], (float)dof[ks][e], part);
+    }
+    delta = pair_sum(part);
+    if (q_ok && g == 0) p.delta[head + q_row] = delta;
+  }
+  const float lse2 = q_ok ? p.lse[head + q_row] * kLog2e : 0.f;
+
+  const int64_t extent = (int64_t)N * RB;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head * RB), (short)0, (int)extent, 0x00020000);
+  int dma_off[LOADS];
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t) {
+    const int pos = (t * NT + tid) * 16;
+    const int row = pos / RB;
+    const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
+    dma_off[t] = row * RB + chunk * 16;
+  }
+  const TileAddr<D> ta(lane);
+
+  f32x16_t dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, m0 + kBwdBlock) : N;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
+  const float c = p.scale_log2;
+
+  auto compute = [&](int j, const char* kt, const char* vt) __attribute__((always_inline)) {
+    f32x16_t sacc[NKB], pacc[NKB];
+    tile_dot<T, D, NKB>(sacc, kt, ta, qf);    // S^T = K Q^T
+    tile_dot<T, D, NKB>(pacc, vt, ta, dof);   // dP^T = V dO^T
+    const int kt0 = j * BN;
+    const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
+    frag dsf[NCC];
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const int kb = cc >> 1, base = (cc & 1) * 8;
+      u32x4_t w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float ds2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = base + 2 * t + u;
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -lse2));
+          if (need_mask) {
+            const int key = kt0 + kb * 32 + key_of_reg(i, g);
+            if ((key >= N) || (CAUSAL && key > q_row)) pr = 0.f;
+          }
+          ds2[u] = pr * (pacc[kb][i] - delta);
+        }
+        w[t] = Op::pack2(ds2[0], ds2[1]);
+      }
+      dsf[cc] = __builtin_bit_cast(frag, w);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc)
+        dqacc[db] = Op::mfma(read_tr<frag, D>(kt + cc * 16 * RB, ta, db), dsf[cc], dqacc[db]);
+  };
+
+  // the tile offset goes into the per-lane offset, which the buffer range
+  // check always covers: rows past N read as zero
+  auto copy = [&](int tile, int st) __attribute__((always_inline)) {
+    int off[LOADS];
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) off[t] = dma_off[t] + tile * BN * RB;
+    dma_tile<LOADS, NT>(krs, st ? sk1 : sk0, wave, 0, off);
+    dma_tile<LOADS, NT>(vrs, st ? sv1 : sv0, wave, 0, off);
+  };
+  auto step = [&](int j, int st) __attribute__((always_inline)) {
+    if (j + 1 < n_tiles) copy(j + 1, st ^ 1);
+    if (j < w_tiles) compute(j, st ? sk1 : sk0, st ? sv1 : sv0);
+    wait_vmem();
+    __syncthreads();
+  };
+  if (n_tiles > 0) copy(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < n_tiles) step(j + 1, 1);
+  }
+
+  if (q_ok) store_rowT<T, D>(p.dq + row_off, dqacc, p.scale, g);
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV.  Grid: (b, h, 128-key block), XCD-grouped per head; under the
+// causal mask the low key blocks (most Q tiles) come first in natural order.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
+  using Op = Ops<T>;
+  using frag = typename Op::frag;
+  constexpr int NT = kBwdThreads, BN = kBwdTile;
+  constexpr int RB = D * 2;
+  constexpr int TILE = BN * RB;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int LOADS = TILE / (NT * 16);
+  static_assert(TILE % (NT * 16) == 0, "tile split");
+
+  __shared__ __attribute__((aligned(1024))) char sq0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sq1[TILE];
+  __shared__ __attribute__((aligned(1024))) char so0[TILE];
+  __shared__ __attribute__((aligned(1024))) char so1[TILE];
+  // per Q tile: LSE (64 floats) then D (64 floats)
+  __shared__ __attribute__((aligned(16))) float st0[2 * BN];
+  __shared__ __attribute__((aligned(16))) float st1[2 * BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int N = p.N;
+
+  const int logical = xcd_logical_id(blockIdx.x, p.total);
+  const int bh = logical / p.nblk;
+  const int kblk = logical - bh * p.nblk;
+  const int k0 = kblk * kBwdBlock;
+  const int wk0 = k0 + wave * 32;
+  const int key = wk0 + n;
+  const bool k_ok = key < N;
+  const int64_t head = (int64_t)bh * N;
+  const int64_t row_off = (head + key) * RB;
+
+  frag kf[NKS], vf[NKS];
+  load_row_frags<T, D>(kf, p.k + row_off, k_ok, g);
+  load_row_frags<T, D>(vf, p.v + row_off, k_ok, g);
+
+  const int64_t extent = (int64_t)N * RB;
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ors =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + head), (short)0, N * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + head), (short)0, N * 4, 0x00020000);
+  int dma_off[LOADS];
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t) {
+    const int pos = (t * NT + tid) * 16;
+    const int row = pos / RB;
+    const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
+    dma_off[t] = row * RB + chunk * 16;
+  }
+  const TileAddr<D> ta(lane);
+
+  f32x16_t dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  const int n_qt = (N + BN - 1) / BN;
+  const int qt_begin = CAUSAL ? k0 / BN : 0;
+  const float c = p.scale_log2;
+
+  // one 32-query block qb (queries q0 .. q0 + 31) of the tile in (qt, ot, sts)
+  auto block = [&](int q0, int qb, const char* qt, const char* ot, const float* sts) __attribute__((always_inline)) {
+    f32x16_t sacc[1], pacc[1];
+    const char* qrows = qt + qb * 32 * RB;
+    const char* orows = ot + qb * 32 * RB;
+    tile_dot<T, D, 1>(sacc, qrows, ta, kf);    // S = Q K^T   (lane = key)
+    tile_dot<T, D, 1>(pacc, orows, ta, vf);    // dP = dO V^T
+    // LSE and D of the 16 queries of this lane's registers: register i holds
+    // query q0 + 16 (i >> 3) + 8 g + (i & 7)
+    float ls[16], dl[16];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int v4 = 0; v4 < 2; ++v4) {
+        const int idx = qb * 32 + 16 * h2 + 8 * g + 4 * v4;
+        const f32x4_t a = *(const f32x4_t*)(sts + idx);
+        const f32x4_t b = *(const f32x4_t*)(sts + BN + idx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ls[8 * h2 + 4 * v4 + e] = a[e] * kLog2e;
+          dl[8 * h2 + 4 * v4 + e] = b[e];
+        }
+      }
+    const bool need_mask = (q0 + 32 > N) || (CAUSAL && q0 < wk0 + 31);
+    frag pf[2], dsf[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4_t wp, wd;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float pr2[2], ds2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = cc * 8 + 2 * t + u;
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], c, -ls[i]));
+          if (need_mask) {
+            const int qi = q0 + key_of_reg(i, g);
+            if ((qi >= N) || (CAUSAL && key > qi)) pr = 0.f;
+          }
+          pr2[u] = pr;
+          ds2[u] = pr * (pacc[0][i] - dl[i]);
+        }
+        wp[t] = Op::pack2(pr2[0], pr2[1]);
+        wd[t] = Op::pack2(ds2[0], ds2[1]);
+      }
+      pf[cc] = __builtin_bit_cast(frag, wp);
+      dsf[cc] = __builtin_bit_cast(frag, wd);
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        dvacc[db] = Op::mfma(read_tr<frag, D>(orows + cc * 16 * RB, ta, db), pf[cc], dvacc[db]);
+        dkacc[db] = Op::mfma(read_tr<frag, D>(qrows + cc * 16 * RB, ta, db), dsf[cc], dkacc[db]);
+      }
+  };
+
+  // tile offsets go into the per-lane offsets, which the buffer range check
+  // always covers: rows (and LSE / D entries) past N read as zero
+  auto copy = [&](int tile, int st) __attribute__((always_inline)) {
+    int off[LOADS];
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) off[t] = dma_off[t] + tile * BN * RB;
+    dma_tile<LOADS, NT>(qrs, st ? sq1 : sq0, wave, 0, off);
+    dma_tile<LOADS, NT>(ors, st ? so1 : so0, wave, 0, off);
+    // the tile's LSE (wave 0) and D (wave 1): 64 floats, one per lane
+    float* sts = st ? st1 : st0;
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void_t*)sts, 4, (tile * BN + lane) * 4, 0, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void_t*)(sts + BN), 4, (tile * BN + lane) * 4, 0, 0, 0);
+  };
+  auto step = [&](int j, int st) __attribute__((always_inline)) {
+    if (j + 1 < n_qt) copy(j + 1, st ^ 1);
+    if (wk0 < N) {   // wave-uniform: the wave has at least one key
+      const int qt0 = j * BN;
+#pragma unroll
+      for (int qb = 0; qb < BN / 32; ++qb) {
+        const int q0 = qt0 + qb * 32;
+        // causal: a block whose last query precedes the wave's first key is all masked
+        if (!CAUSAL || q0 + 31 >= wk0)
+          block(q0, qb, st ? sq1 : sq0, st ? so1 : so0, st ? st1 : st0);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  if (qt_begin < n_qt) copy(qt_begin, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = qt_begin; j < n_qt; j += 2) {
+    step(j, 0);
+    if (j + 1 < n_qt) step(j + 1, 1);
+  }
+
+  if (k_ok) {
+    store_rowT<T, D>(p.dk + row_off, dkacc, p.scale, g);
+    store_rowT<T, D>(p.dv + row_off, dvacc, 1.f, g);
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const char*>(a.q);
+  p.k = static_cast<const char*>(a.k);
+  p.v = static_cast<const char*>(a.v);
+  p.o = static_cast<const char*>(a.o);
+  p.dout = static_cast<const char*>(a.dout);
+  p.lse = a.lse;
+  p.delta = a.delta;
+  p.dq = static_cast<char*>(a.dq);
+  p.dk = static_cast<char*>(a.dk);
+  p.dv = static_cast<char*>(a.dv);
+  p.N = a.N;
+  p.nblk = (a.N + kBwdBlock - 1) / kBwdBlock;
+  p.total = a.B * a.H * p.nblk;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, bool* ok) {
+  *ok = true;
+  switch (a.d) {
+    case 64: return a.causal ? launch_bwd<T, 64, true>(a, s) : launch_bwd<T, 64, false>(a, s);
+    case 128: return a.causal ? launch_bwd<T, 128, true>(a, s) : launch_bwd<T, 128, false>(a, s);
+  }
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream, bool* supported) {
+  switch (a.dtype) {
+    case Dtype::BF16: return launch_bwd_t<__bf16>(a, stream, supported);
+    case Dtype::F16: return launch_bwd_t<_Float16>(a, stream, supported);
+    default: break;
+  }
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace attn

@@ -64,6 +64,23 @@ struct Fp8FwdArgs {
   bool causal;
 };
 
+struct BwdArgs {
+  Dtype dtype;          // F16 or BF16
+  int B, H, N, d;
+  const void* q;        // contiguous [B, H, N, d]
+  const void* k;
+  const void* v;
+  const void* o;        // forward output
+  const void* dout;     // upstream gradient dO
+  const float* lse;     // forward LSE [B, H, N]
+  float* delta;         // workspace [B, H, N]: dO . O per row
+  void* dq;             // outputs, contiguous [B, H, N, d], dtype of q
+  void* dk;
+  void* dv;
+  float scale;
+  bool causal;
+};
+
 // Each returns hipSuccess or the launch error.  `supported` is set false
 // (and nothing launched) when no instantiation covers the request.
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream, bool* supported);
@@ -72,5 +89,7 @@ hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* su
 // split-KV partials (bf16 / fp16, d = 64 and 128) and their merge
 hipError_t launch_attn_fwd16_pp_split(const FwdArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream, bool* supported);
+// backward: dq kernel (also writes delta) then dk/dv kernel (fp16 / bf16, d = 64 and 128)
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream, bool* supported);
 
 }  // namespace attn

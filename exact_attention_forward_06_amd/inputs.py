@@ -116,6 +116,15 @@ def workload_inputs(w: Workload | str):
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.outlier_frac, w.outlier_gain)
 
 
+def upstream_grad(B, H, N, d, dtype="bf16", seed=0):
+    """The backward's upstream gradient dO [B,H,N,d]: i.i.d. N(0, 1) in
+    float32 from its own PCG64 stream (seed sequence [seed, 1]), so the Q, K,
+    V of make_inputs(..., seed) are unchanged, cast to the storage dtype."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1]))
+    g = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    return torch.from_numpy(g).to(storage_dtype(dtype))
+
+
 def random_signs(d: int, seed: int) -> torch.Tensor:
     rng = np.random.Generator(np.random.PCG64(seed))
     return torch.from_numpy((rng.integers(0, 2, d) * 2 - 1).astype(np.int8))

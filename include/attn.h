@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum {
@@ -239,6 +239,44 @@ int attn_fwd_fp8(int B, int H, int N, int d,
                  int block_rows, int fp8_format,
                  void* o, float* lse,
                  float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_bwd -- gradients of the exact attention of attn_fwd:
+ *     dV = P^T dO,   dS = P o (dO V^T - D),   D_i = dO_i . O_i,
+ *     dQ = softmax_scale dS K,   dK = softmax_scale dS^T Q,
+ * with P = exp(softmax_scale Q K^T - LSE) recomputed tile by tile from the
+ * forward's logsumexp, so no N x N matrix reaches device memory.  Sources:
+ * the backward pass is named on the "FlashAttention-3" page (section
+ * "适用范围和工程限制", fp16/bf16 forward and backward) and its recomputation
+ * of P from the saved softmax statistics (the LSE) on the "Flash Attention
+ * V3" page, sections 2.1 and 2.2; the formulas are the chain rule through
+ * the attention definition of the "FlashAttention-3" page.
+ *
+ *   dtype          ATTN_F16 or ATTN_BF16 (ATTN_F32: ATTN_ERR_UNSUPPORTED):
+ *                  type of q, k, v, o, dout, dq, dk, dv.
+ *   B, H, N, d     as in attn_fwd; d in {64, 128} (256: ATTN_ERR_UNSUPPORTED).
+ *   q, k, v        device [B, H, N, d] forward inputs, contiguous.
+ *   o, lse         device forward outputs of attn_fwd on the same q, k, v,
+ *                  softmax_scale and causal: o [B, H, N, d] contiguous,
+ *                  lse fp32 [B, H, N].
+ *   dout           device [B, H, N, d] upstream gradient dO, contiguous.
+ *   delta          device fp32 [B, H, N] caller-owned workspace; the call
+ *                  overwrites it with D_i = dO_i . O_i (fp32 sums of the
+ *                  16-bit products) and keeps no pointer to it.
+ *   dq, dk, dv     device [B, H, N, d] outputs, contiguous, same dtype.
+ *   softmax_scale, causal, stream   as in attn_fwd.
+ *
+ * Two launches on `stream` in order (dQ and D first, then dK and dV); no
+ * atomics, so the result is bitwise reproducible.  Accumulation is fp32;
+ * P and dS are rounded to the input dtype as operands of the second
+ * products, and each gradient is rounded to the dtype once at the end.
+ * Outputs and the workspace must not overlap each other or the inputs.
+ */
+int attn_bwd(int dtype, int B, int H, int N, int d,
+             const void* q, const void* k, const void* v,
+             const void* o, const float* lse, const void* dout,
+             float* delta, void* dq, void* dk, void* dv,
+             float softmax_scale, int causal, void* stream);
 
 #ifdef __cplusplus
 }

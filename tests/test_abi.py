@@ -34,10 +34,11 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
-                          "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge"}
+                          "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge",
+                          "attn_bwd"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -173,6 +174,42 @@ def _merge(lib, dtype=2, S=3, B=1, H=2, N=100, d=64, op=OP, lp=LP, o=O, lse=L):
 ])
 def test_merge_rejects(lib, kw, status, msg):
     assert _merge(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+# backward: eight [B, H, N, d] / [B, H, N] buffers at distinct fake addresses
+BW = {name: 0x100000000 + i * 0x10000000 for i, name in
+      enumerate(("q", "k", "v", "o", "lse", "dout", "delta", "dq", "dk", "dv"))}
+
+
+def _bwd(lib, dtype=2, B=1, H=2, N=100, d=128, scale=0.125, causal=0, **ptrs):
+    p = dict(BW, **ptrs)
+    return lib.attn_bwd(dtype, B, H, N, d, p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["delta"],
+                        p["dq"], p["dk"], p["dv"], scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(dout=None), 1, "dout is NULL"),
+    (dict(delta=None), 1, "delta is NULL"),
+    (dict(dv=None), 1, "dv is NULL"),
+    (dict(dq=BW["dq"] + 8), 1, "not 16-byte aligned"),
+    (dict(lse=BW["lse"] + 2), 1, "not 4-byte aligned"),
+    (dict(N=0), 1, "sizes must be positive"),
+    (dict(dtype=0), 2, "fp16 / bf16"),
+    (dict(d=256), 2, "fp16 / bf16"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(dtype=7), 1, "unknown dtype"),
+    (dict(scale=0.0), 1, "softmax_scale"),
+    (dict(causal=2), 1, "causal"),
+    (dict(dq=BW["q"] + 0x100), 1, "overlaps an input"),
+    (dict(delta=BW["lse"]), 1, "overlaps an input"),
+    (dict(dk=BW["dq"] + 0x200), 1, "outputs overlap"),
+    (dict(delta=BW["dv"] + 0x40), 1, "outputs overlap"),
+])
+def test_bwd_rejects(lib, kw, status, msg):
+    assert _bwd(lib, **kw) == status
     assert msg in lib.attn_last_error().decode()
 
 
