@@ -26,6 +26,10 @@
 //    B operand of v_mfma_f32_32x32x16_{bf16,f16} in VGPRs (dq: Q and dO;
 //    dkdv: K and V).  The streamed 64-row tiles go global -> LDS with
 //    buffer_load ... lds, double-buffered, into the XOR-swizzled row layout.
+//    The dq kernel (and dkdv at d = 64) fits 256 VGPRs, so two workgroups
+//    share a CU and each SIMD interleaves two waves' VALU and MFMA work; the
+//    dkdv kernel at d = 128 holds K, V, dK and dV (192 registers) besides the
+//    tile products and runs one wave per SIMD with its accumulators in AGPRs.
 //  * dq kernel: S^T = K Q^T and dP^T = V dO^T (lane = one query, registers =
 //    16 of the tile's keys, key order permuted so registers 8c..8c+7 hold 8
 //    consecutive keys); dS^T rounded to 16 bits is directly the B operand of
@@ -165,7 +169,7 @@ __device__ __forceinline__ void store_rowT(char* dst, const f32x16_t (&acc)[D / 
 // dQ (and D_i).  Grid: (b, h, 128-query block), XCD-grouped per head; under
 // the causal mask the blocks with the most K/V tiles go first.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(BwdParams p) {
   using Op = Ops<T>;
   using frag = typename Op::frag;
@@ -243,15 +247,24 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
   const int kv_end = CAUSAL ? min(N, m0 + kBwdBlock) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
-  const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
   const float c = p.scale_log2;
 
   auto compute = [&](int j, const char* kt, const char* vt) __attribute__((always_inline)) {
     f32x16_t sacc[NKB], pacc[NKB];
     tile_dot<T, D, NKB>(sacc, kt, ta, qf);    // S^T = K Q^T
     tile_dot<T, D, NKB>(pacc, vt, ta, dof);   // dP^T = V dO^T
+    // masked scores -> -inf (P = 0, dS = 0), only on tiles that straddle
+    // the diagonal or the end of the sequence
     const int kt0 = j * BN;
-    const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
+    if ((kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 + kb * 32 + key_of_reg(i, g);
+          if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
+        }
+    }
     frag dsf[NCC];
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
@@ -263,11 +276,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = base + 2 * t + u;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -lse2));
-          if (need_mask) {
-            const int key = kt0 + kb * 32 + key_of_reg(i, g);
-            if ((key >= N) || (CAUSAL && key > q_row)) pr = 0.f;
-          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -lse2));
           ds2[u] = pr * (pacc[kb][i] - delta);
         }
         w[t] = Op::pack2(ds2[0], ds2[1]);
@@ -291,9 +300,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
     dma_tile<LOADS, NT>(krs, st ? sk1 : sk0, wave, 0, off);
     dma_tile<LOADS, NT>(vrs, st ? sv1 : sv0, wave, 0, off);
   };
+  // Every wave runs every tile of its workgroup: a tile past a wave's last
+  // query (causal) is wholly masked and adds zero.  (Skipping it per wave
+  // would put the dQ accumulator under control flow, which the compiler
+  // answers with a copy of the whole accumulator at every tile.)
   auto step = [&](int j, int st) __attribute__((always_inline)) {
     if (j + 1 < n_tiles) copy(j + 1, st ^ 1);
-    if (j < w_tiles) compute(j, st ? sk1 : sk0, st ? sv1 : sv0);
+    compute(j, st ? sk1 : sk0, st ? sv1 : sv0);
     wait_vmem();
     __syncthreads();
   };
@@ -312,7 +325,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 // dK and dV.  Grid: (b, h, 128-key block), XCD-grouped per head; under the
 // causal mask the low key blocks (most Q tiles) come first in natural order.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1, D <= 64 ? 2 : 1)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
   using Op = Ops<T>;
   using frag = typename Op::frag;
@@ -407,7 +420,15 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
           dl[8 * h2 + 4 * v4 + e] = b[e];
         }
       }
-    const bool need_mask = (q0 + 32 > N) || (CAUSAL && q0 < wk0 + 31);
+    // masked scores -> -inf (P = 0, dS = 0), only on blocks that straddle
+    // the diagonal or the end of the sequence
+    if ((q0 + 32 > N) || (CAUSAL && q0 < wk0 + 31)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = q0 + key_of_reg(i, g);
+        if ((qi >= N) || (CAUSAL && key > qi)) sacc[0][i] = -INFINITY;
+      }
+    }
     frag pf[2], dsf[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
@@ -418,11 +439,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = cc * 8 + 2 * t + u;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], c, -ls[i]));
-          if (need_mask) {
-            const int qi = q0 + key_of_reg(i, g);
-            if ((qi >= N) || (CAUSAL && key > qi)) pr = 0.f;
-          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], c, -ls[i]));
           pr2[u] = pr;
           ds2[u] = pr * (pacc[0][i] - dl[i]);
         }
@@ -457,18 +474,15 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     else if (wave == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void_t*)(sts + BN), 4, (tile * BN + lane) * 4, 0, 0, 0);
   };
+  // Every wave runs every block of its workgroup's tiles: a block before a
+  // wave's first key (causal) or a wave past N is wholly masked or never
+  // stored.  (Skipping per wave would put the dK / dV accumulators under
+  // control flow, which the compiler answers with copies of them.)
   auto step = [&](int j, int st) __attribute__((always_inline)) {
     if (j + 1 < n_qt) copy(j + 1, st ^ 1);
-    if (wk0 < N) {   // wave-uniform: the wave has at least one key
-      const int qt0 = j * BN;
 #pragma unroll
-      for (int qb = 0; qb < BN / 32; ++qb) {
-        const int q0 = qt0 + qb * 32;
-        // causal: a block whose last query precedes the wave's first key is all masked
-        if (!CAUSAL || q0 + 31 >= wk0)
-          block(q0, qb, st ? sq1 : sq0, st ? so1 : so0, st ? st1 : st0);
-      }
-    }
+    for (int qb = 0; qb < BN / 32; ++qb)
+      block(j * BN + qb * 32, qb, st ? sq1 : sq0, st ? so1 : so0, st ? st1 : st0);
     wait_vmem();
     __syncthreads();
   };
