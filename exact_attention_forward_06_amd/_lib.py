@@ -35,6 +35,8 @@ _SIGNATURES = {
     "attn_fwd_splitkv": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                           ctypes.c_float, _i, _vp], _i),
     "attn_merge": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
+    "rope_hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.c_double, _i, _vp, _i, _i, _vp,
+                                    _vp, _vp], _i),
     "attn_bwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                   _i, _vp], _i),
 }
@@ -187,6 +189,34 @@ def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, ou
     _check(lib.hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides,
                                      _ptr(signs), block_rows, FP8_FORMATS[fp8_format],
                                      int(bool(transpose_out)), _ptr(out), _ptr(scales), _stream(stream)))
+    return out, scales
+
+
+ROPE_STYLES = {"interleaved": 1, "half": 2}
+
+
+def rope_hadamard_rotate_quant(x, signs=None, style="interleaved", base=10000.0, pos_offset=0, block_rows=128,
+                               out=None, scales=None, stream=None, fp8_format="e4m3"):
+    """FP8 pre-pass of Q or K with RoPE in front: rows at positions
+    pos_offset + n are rotary-embedded (pairs (2i, 2i+1) for "interleaved",
+    (i, i + d/2) for "half", angle n * base^(-2i/d)), then optionally rotated
+    by (1/sqrt(d)) H diag(signs), then block-quantised.
+    Returns (codes uint8 [B,H,N,d], scales fp32 [B,H,nblk])."""
+    lib = load()
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError("x must be fp32, fp16 or bf16")
+    B, H, N, d = x.shape
+    strides = _bhnd_strides(x)
+    nblk = -(-N // block_rows)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    if signs is not None and signs.dtype != torch.int8:
+        raise ValueError("signs must be int8")
+    _check(lib.rope_hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides, ROPE_STYLES[style],
+                                          float(base), int(pos_offset), _ptr(signs), block_rows,
+                                          FP8_FORMATS[fp8_format], _ptr(out), _ptr(scales), _stream(stream)))
     return out, scales
 
 

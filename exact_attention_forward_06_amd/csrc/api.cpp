@@ -342,6 +342,60 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* 
   return hip_status(e, "hadamard_rotate_quant launch");
 }
 
+int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,
+                               const int64_t* x_strides, int rope_style, double rope_base,
+                               int pos_offset, const int8_t* signs, int block_rows, int fp8_format,
+                               uint8_t* x8, float* scales, void* stream) {
+  const int es = elem_size(in_dtype);
+  if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", in_dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
+  if (fp8_format != ATTN_FP8_E4M3 && fp8_format != ATTN_FP8_E5M2)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown fp8_format %d", fp8_format);
+  if (rope_style != ATTN_ROPE_INTERLEAVED && rope_style != ATTN_ROPE_HALF)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown rope_style %d", rope_style);
+  if (!std::isfinite(rope_base) || !(rope_base >= 1.0))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "rope_base must be finite and at least 1");
+  if (pos_offset < 0 || (int64_t)pos_offset + N > INT32_MAX)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "positions pos_offset .. pos_offset + N - 1 must lie in 0 .. 2^31 - 1");
+  int64_t sb, sh, sn;
+  strides_or_contiguous(x_strides, H, N, d, &sb, &sh, &sn);
+  const int nblk = (N + block_rows - 1) / block_rows;
+  Span sx, s8, ss, sg{0, 0};
+  if (int st = check_strided("x", x, B, H, N, d, sb, sh, sn, es, &sx)) return st;
+  if (int st = check_dense("x8", x8, (int64_t)B * H * N * d, &s8)) return st;
+  if (int st = check_dense("scales", scales, (int64_t)B * H * nblk * 4, &ss, false)) return st;
+  if (signs) {
+    if (int st = check_dense("signs", signs, d, &sg, false)) return st;
+  }
+  if (overlaps(s8, sx) || overlaps(ss, sx) || overlaps(s8, ss) || (signs && (overlaps(sg, s8) || overlaps(sg, ss))))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs overlap inputs or each other");
+
+  attn::QuantArgs a;
+  a.dtype = static_cast<attn::Dtype>(in_dtype);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.x = x;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.signs = signs;
+  a.block_rows = block_rows;
+  a.fp8_format = fp8_format;
+  a.transpose_out = false;
+  a.x8 = x8;
+  a.scales = scales;
+  a.rope_style = rope_style;
+  a.rope_base = rope_base;
+  a.pos_offset = pos_offset;
+  bool supported = true;
+  hipError_t e = attn::launch_hadamard_rotate_quant(a, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no rope_hadamard_rotate_quant kernel for d=%d", d);
+  return hip_status(e, "rope_hadamard_rotate_quant launch");
+}
+
 int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_scale,
                  const uint8_t* k8, const float* k_scale, const uint8_t* v8t, const float* v_scale,
                  int block_rows, int fp8_format, void* o, float* lse, float softmax_scale,

@@ -30,6 +30,18 @@
 //    share the significand 1.75, so the quotient stays exact alike.
 //  * transpose_out writes [d][n] (the layout the FP8 attention kernel wants
 //    for V): codes are transposed through LDS so global stores stay 16-byte.
+//  * RoPE (ROPE = 1: pairs (2i, 2i+1); ROPE = 2: pairs (i, i + d/2)) runs on
+//    the loaded fp32 values before D and H, so the producer pass that the
+//    "FlashAttention-3" page suggests (Hadamard fused with a bandwidth-bound
+//    pre-processing stage such as RoPE, section "为什么 Hadamard 适合放到内核里")
+//    still reads x once and writes the codes once.  RoPE itself is the
+//    published rotary embedding (RoFormer): pair i at position n turns by
+//    n * theta_i, theta_i = base^(-2i/d).  The theta_i come from the host in
+//    double; n * theta_i is formed and reduced by pi/2 in fp64 (an fp32
+//    angle near n = 8192 would be off by up to 5e-4 rad), then sin and cos of
+//    the reduced angle by their Taylor series in fp32.  Interleaved pairs sit in one lane; split-half
+//    pairs are lanes l and l ^ 2, exchanged by the same DPP swap as the
+//    butterflies.
 #include "kernels.h"
 
 #include <math.h>
@@ -55,6 +67,55 @@ struct QParams {
   float scale_norm;   // 1/sqrt(d) for the rotated path, 1 otherwise
 };
 
+// RoPE angle table (ROPE != 0 only): theta_i = base^(-2i/d), i < d/2
+struct RopeTab {
+  double theta[128];
+  int pos_offset;
+};
+struct NoRope {
+  int unused;
+};
+template <int ROPE>
+struct RopeArg {
+  using type = RopeTab;
+};
+template <>
+struct RopeArg<0> {
+  using type = NoRope;
+};
+
+// theta of one of NC equally spaced table entries, picked per lane: every
+// index is a compile-time constant (scalar loads from the kernel arguments;
+// a per-lane index would copy the table to scratch)
+template <int NC, int STRIDE>
+__device__ __forceinline__ double pick_theta(const RopeTab& rt, int k, int sel) {
+  double t = rt.theta[k];
+#pragma unroll
+  for (int c = 1; c < NC; ++c)
+    if (sel == c) t = rt.theta[c * STRIDE + k];
+  return t;
+}
+
+// sin and cos of a non-negative angle (pos * theta, below 2^31 since
+// theta <= 1): reduction by pi/2 in fp64 to t in [-pi/4, pi/4] and the
+// quadrant q, then the Taylor series of sin t (to t^9) and cos t (to t^10) in
+// fp32 -- the first omitted terms are below 2e-9 on that interval -- and a
+// quarter-turn rotation by q.
+__device__ __forceinline__ void rope_sincos(double ang, float* sn, float* cs) {
+  const double k = rint(ang * 0.63661977236758134);            // 2 / pi
+  const float t = (float)fma(-k, 1.5707963267948966, ang);       // pi / 2
+  const float t2 = t * t;
+  const float st = t * fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, 1.f / 362880.f, -1.f / 5040.f), 1.f / 120.f),
+                                     -1.f / 6.f), 1.f);
+  const float ct = fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, -1.f / 3628800.f, 1.f / 40320.f), -1.f / 720.f),
+                                           1.f / 24.f), -0.5f), 1.f);
+  const int q = (int)k & 3;
+  const float a = (q & 1) ? ct : st;      // sin(t + q pi/2) up to sign
+  const float b = (q & 1) ? st : ct;      // cos(t + q pi/2) up to sign
+  *sn = (q & 2) ? -a : a;
+  *cs = ((q + 1) & 2) ? -b : b;
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);
 template <>
@@ -77,8 +138,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-template <typename T, int D, bool ROT, bool TRANS, int FMT>
-__global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
+template <typename T, int D, bool ROT, bool TRANS, int FMT, int ROPE = 0>
+__global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p, typename RopeArg<ROPE>::type rt) {
+  static_assert(!(ROPE && TRANS), "RoPE applies to Q and K, which are not transposed");
   constexpr float QMAX = FMT == 0 ? 448.f : 57344.f;   // largest finite E4M3 / E5M2 value
   constexpr int EPL = D / LPR;                  // elements per lane
   constexpr int ES = sizeof(T);
@@ -118,6 +180,30 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p) {
       const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
       for (int t = 0; t < PER16; ++t) v[ps][l * PER16 + t] = to_f32<T>(e[t]);
+    }
+    if constexpr (ROPE == 1) {
+      // pairs (2i, 2i + 1), i = lane's first pair + k
+      const double pos = (double)(rt.pos_offset + row);
+#pragma unroll
+      for (int k = 0; k < EPL / 2; ++k) {
+        float sn, cs;
+        rope_sincos(pos * pick_theta<LPR, EPL / 2>(rt, k, lr), &sn, &cs);
+        const float a = v[ps][2 * k], c = v[ps][2 * k + 1];
+        v[ps][2 * k] = a * cs - c * sn;
+        v[ps][2 * k + 1] = a * sn + c * cs;
+      }
+    } else if constexpr (ROPE == 2) {
+      // pairs (i, i + d/2): lanes 0, 1 hold the first members, lanes 2, 3
+      // (the partners at lane ^ 2, same k) the second
+      const double pos = (double)(rt.pos_offset + row);
+      const bool second = lr & 2;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        float sn, cs;
+        rope_sincos(pos * pick_theta<2, EPL>(rt, k, lr & 1), &sn, &cs);
+        const float o = xor2(v[ps][k]);
+        v[ps][k] = second ? o * sn + v[ps][k] * cs : v[ps][k] * cs - o * sn;
+      }
     }
     if constexpr (ROT) {
       // D: sign flip
@@ -233,12 +319,27 @@ hipError_t launch_f(const QuantArgs& a, hipStream_t s) {
   p.nblk = (a.N + ROWS - 1) / ROWS;
   p.scale_norm = a.signs ? 1.f / sqrtf((float)D) : 1.f;
   dim3 grid(p.nblk, a.B * a.H);
+  if (a.rope_style != 0) {
+    RopeTab rt;
+    for (int i = 0; i < D / 2; ++i) rt.theta[i] = pow(a.rope_base, -2.0 * i / D);
+    for (int i = D / 2; i < 128; ++i) rt.theta[i] = 0.0;
+    rt.pos_offset = a.pos_offset;
+    if (a.rope_style == 1) {
+      if (a.signs) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false, FMT, 1>), grid, dim3(NT), 0, s, p, rt);
+      else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false, FMT, 1>), grid, dim3(NT), 0, s, p, rt);
+    } else {
+      if (a.signs) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false, FMT, 2>), grid, dim3(NT), 0, s, p, rt);
+      else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false, FMT, 2>), grid, dim3(NT), 0, s, p, rt);
+    }
+    return hipGetLastError();
+  }
+  const NoRope nr{0};
   if (a.signs) {
-    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, true, FMT>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false, FMT>), grid, dim3(NT), 0, s, p);
+    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, true, FMT>), grid, dim3(NT), 0, s, p, nr);
+    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, true, false, FMT>), grid, dim3(NT), 0, s, p, nr);
   } else {
-    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, true, FMT>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false, FMT>), grid, dim3(NT), 0, s, p);
+    if (a.transpose_out) hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, true, FMT>), grid, dim3(NT), 0, s, p, nr);
+    else hipLaunchKernelGGL((hadamard_quant_kernel<T, D, false, false, FMT>), grid, dim3(NT), 0, s, p, nr);
   }
   return hipGetLastError();
 }
@@ -263,7 +364,8 @@ hipError_t launch_t(const QuantArgs& a, hipStream_t s, bool* ok) {
 }  // namespace
 
 hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported) {
-  if (a.block_rows != ROWS || (a.fp8_format != 0 && a.fp8_format != 1)) {
+  if (a.block_rows != ROWS || (a.fp8_format != 0 && a.fp8_format != 1) || a.rope_style < 0 || a.rope_style > 2 ||
+      (a.rope_style != 0 && a.transpose_out)) {
     *supported = false;
     return hipSuccess;
   }

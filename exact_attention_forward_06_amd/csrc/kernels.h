@@ -46,6 +46,10 @@ struct QuantArgs {
   bool transpose_out;
   uint8_t* x8;
   float* scales;
+  // RoPE before the rotation: 0 none, 1 pairs (2i, 2i+1), 2 pairs (i, i + d/2)
+  int rope_style = 0;
+  double rope_base = 10000.0;
+  int pos_offset = 0;   // position of row 0
 };
 
 struct Fp8FwdArgs {

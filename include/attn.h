@@ -240,6 +240,40 @@ int attn_fwd_fp8(int B, int H, int N, int d,
                  void* o, float* lse,
                  float softmax_scale, int causal, void* stream);
 
+/* Pairings of rope_hadamard_rotate_quant. */
+enum { ATTN_ROPE_INTERLEAVED = 1, ATTN_ROPE_HALF = 2 };
+
+/*
+ * rope_hadamard_rotate_quant -- the FP8 pre-pass of Q or K with rotary
+ * position embedding fused in front: per row x at position n,
+ *     x~ = (1/sqrt(d)) H D RoPE_n(x)        (signs given; RoPE_n(x) if NULL)
+ * then per-128-row-block codes and scales exactly as hadamard_rotate_quant.
+ * Source: the "FlashAttention-3" page, section "为什么 Hadamard 适合放到内核里",
+ * suggests fusing the Hadamard transform with a bandwidth-bound
+ * pre-processing stage such as RoPE; the page gives no RoPE formula, so
+ * RoPE is the published rotary embedding (RoFormer, Su et al.): pair i of
+ * the row turns by the angle n * theta_i, theta_i = rope_base^(-2i/d),
+ *     (a, b) -> (a cos - b sin, a sin + b cos).
+ *
+ *   in_dtype, B, H, N, d, x, x_strides, signs, block_rows, fp8_format, x8,
+ *   scales, stream   as in hadamard_rotate_quant (codes in [B, H, N, d]
+ *                  order only: V, the transposed tensor, has no RoPE).
+ *   rope_style     ATTN_ROPE_INTERLEAVED: pairs (x[2i], x[2i+1]);
+ *                  ATTN_ROPE_HALF: pairs (x[i], x[i + d/2]).
+ *   rope_base      finite, >= 1 (10000 in common use), so theta_i <= 1.
+ *   pos_offset     position of row 0 (rows of every (b, h) are positions
+ *                  pos_offset .. pos_offset + N - 1); pos_offset >= 0 and
+ *                  pos_offset + N <= 2^31 - 1.
+ *
+ * theta_i is computed in double on the host; n * theta_i is reduced by
+ * pi/2 in fp64 on the device; sin, cos and the rotation run in fp32.
+ */
+int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
+                               const void* x, const int64_t* x_strides,
+                               int rope_style, double rope_base, int pos_offset,
+                               const int8_t* signs, int block_rows, int fp8_format,
+                               uint8_t* x8, float* scales, void* stream);
+
 /*
  * attn_bwd -- gradients of the exact attention of attn_fwd:
  *     dV = P^T dO,   dS = P o (dO V^T - D),   D_i = dO_i . O_i,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge",
-                          "attn_bwd"}
+                          "attn_bwd", "rope_hadamard_rotate_quant"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_abi_version() == 3
@@ -210,6 +210,32 @@ def _bwd(lib, dtype=2, B=1, H=2, N=100, d=128, scale=0.125, causal=0, **ptrs):
 ])
 def test_bwd_rejects(lib, kw, status, msg):
     assert _bwd(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def _rope(lib, dtype=2, B=1, H=1, N=256, d=128, x=A, style=1, base=10000.0, off=0, signs=B_, block_rows=128,
+          fmt=0, x8=C, sc=O):
+    return lib.rope_hadamard_rotate_quant(dtype, B, H, N, d, x, None, style, base, off, signs, block_rows, fmt,
+                                          x8, sc, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(style=0), 1, "rope_style"),
+    (dict(style=3), 1, "rope_style"),
+    (dict(base=0.5), 1, "rope_base"),
+    (dict(base=float("inf")), 1, "rope_base"),
+    (dict(base=float("nan")), 1, "rope_base"),
+    (dict(off=-1), 1, "pos_offset"),
+    (dict(off=2 ** 31 - 100), 1, "pos_offset"),
+    (dict(x=None), 1, "x is NULL"),
+    (dict(x8=A + 0x100), 1, "overlap"),
+    (dict(block_rows=64), 1, "block_rows"),
+    (dict(fmt=2), 1, "fp8_format"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(dtype=9), 1, "unknown dtype"),
+])
+def test_rope_quant_rejects(lib, kw, status, msg):
+    assert _rope(lib, **kw) == status
     assert msg in lib.attn_last_error().decode()
 
 
