@@ -486,8 +486,8 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
       if (overlaps(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs overlap each other");
   }
   // one head's rows are addressed with 32-bit buffer offsets (including up
-  // to one 64-row tile past N, which reads as zero)
-  if (((int64_t)N + 64) * d * es >= ((int64_t)1 << 31))
+  // to one 128-row block past N, which reads as zero)
+  if (((int64_t)N + 128) * d * es >= ((int64_t)1 << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
 
   attn::BwdArgs a;

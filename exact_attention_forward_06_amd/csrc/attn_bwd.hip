@@ -27,9 +27,10 @@
 //    dkdv: K and V).  The streamed 64-row tiles go global -> LDS with
 //    buffer_load ... lds, double-buffered, into the XOR-swizzled row layout.
 //    The dq kernel (and dkdv at d = 64) fits 256 VGPRs, so two workgroups
-//    share a CU and each SIMD interleaves two waves' VALU and MFMA work; the
-//    dkdv kernel at d = 128 holds K, V, dK and dV (192 registers) besides the
-//    tile products and runs one wave per SIMD with its accumulators in AGPRs.
+//    share a CU and each SIMD interleaves two waves' VALU and MFMA work.  At
+//    d = 128, K, V, dK and dV of 32 keys alone take 192 registers, so dK / dV
+//    run in attn_bwd_dkdv8_kernel: K and V stay in LDS, 8 waves, two per
+//    SIMD, each pair splitting the query rows of every tile.
 //  * dq kernel: S^T = K Q^T and dP^T = V dO^T (lane = one query, registers =
 //    16 of the tile's keys, key order permuted so registers 8c..8c+7 hold 8
 //    consecutive keys); dS^T rounded to 16 bits is directly the B operand of
@@ -500,6 +501,232 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK and dV at d = 128 with 8 waves.  K and V of the workgroup's 128 keys
+// stay in LDS and are read as B operands, so a wave holds only its dK / dV
+// accumulators and one block's products (< 256 VGPRs) and two waves share
+// each SIMD.  Waves w and w + 4 own the same 32 keys: wave w takes query rows
+// 0..31 of every 64-row Q tile, wave w + 4 rows 32..63; at the end each pair
+// adds its partial dK and dV through LDS (wave w finishes dK, wave w + 4 dV).
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv8_kernel(BwdParams p) {
+  using Op = Ops<T>;
+  using frag = typename Op::frag;
+  constexpr int NT = 512, BN = kBwdTile;
+  constexpr int RB = D * 2;
+  constexpr int TILE = BN * RB;                  // one Q (or dO) tile
+  constexpr int KVB = kBwdBlock * RB;            // the block's K (or V)
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int LOADS = TILE / (NT * 16);
+  constexpr int KV_LOADS = KVB / (NT * 16);
+  constexpr int XCH = NDB * 16 * 64 * 4;         // one wave's dK (or dV) partial, bytes
+  static_assert(TILE % (NT * 16) == 0 && KVB % (NT * 16) == 0, "tile split");
+  static_assert(4 * XCH <= 2 * KVB && XCH <= TILE, "exchange slots");
+
+  __shared__ __attribute__((aligned(1024))) char skv[2 * KVB];   // K rows, then V rows
+  __shared__ __attribute__((aligned(1024))) char sq0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sq1[TILE];
+  __shared__ __attribute__((aligned(1024))) char so0[TILE];
+  __shared__ __attribute__((aligned(1024))) char so1[TILE];
+  __shared__ __attribute__((aligned(16))) float st0[2 * BN];
+  __shared__ __attribute__((aligned(16))) float st1[2 * BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;          // key group: 32 keys
+  const int qh = wave >> 2;         // query half of each tile
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int N = p.N;
+
+  const int logical = xcd_logical_id(blockIdx.x, p.total);
+  const int bh = logical / p.nblk;
+  const int kblk = logical - bh * p.nblk;
+  const int k0 = kblk * kBwdBlock;
+  const int wk0 = k0 + kg * 32;
+  const int key = wk0 + n;
+  const int64_t head = (int64_t)bh * N;
+
+  const int64_t extent = (int64_t)N * RB;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ors =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + head), (short)0, N * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + head), (short)0, N * 4, 0x00020000);
+
+  // the block's K and V rows (zero past N), swizzled like the tiles
+  {
+    int off[KV_LOADS];
+#pragma unroll
+    for (int t = 0; t < KV_LOADS; ++t) {
+      const int pos = (t * NT + tid) * 16;
+      const int row = pos / RB;
+      off[t] = (k0 + row) * RB + (((pos % RB) / 16) ^ swz<D>(row)) * 16;
+    }
+    dma_tile<KV_LOADS, NT>(krs, skv, wave, 0, off);
+    dma_tile<KV_LOADS, NT>(vrs, skv + KVB, wave, 0, off);
+  }
+  int dma_off[LOADS];
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t) {
+    const int pos = (t * NT + tid) * 16;
+    const int row = pos / RB;
+    dma_off[t] = row * RB + (((pos % RB) / 16) ^ swz<D>(row)) * 16;
+  }
+  const TileAddr<D> ta(lane);
+  // B operand rows of K and V: lane (n, g) reads chunk 2 ks + g of key row kg * 32 + n
+  int kvaddr[NKS];
+  {
+    const int row = kg * 32 + n;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kvaddr[ks] = row * RB + (((2 * ks + g) ^ swz<D>(row)) * 16);
+  }
+
+  f32x16_t dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  const int n_qt = (N + BN - 1) / BN;
+  const int qt_begin = CAUSAL ? k0 / BN : 0;
+  const float c = p.scale_log2;
+
+  // this wave's 32 queries q0 .. q0 + 31 of the tile in (qt, ot, sts)
+  auto block = [&](int q0, const char* qt, const char* ot, const float* sts) __attribute__((always_inline)) {
+    const char* qrows = qt + qh * 32 * RB;
+    const char* orows = ot + qh * 32 * RB;
+    f32x16_t sacc, pacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = 0.f;
+      pacc[i] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(qrows + ta.rows[ks]));
+      const frag b = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(skv + kvaddr[ks]));
+      sacc = Op::mfma(a, b, sacc);                     // S = Q K^T   (lane = key)
+      const frag a2 = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(orows + ta.rows[ks]));
+      const frag b2 = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(skv + KVB + kvaddr[ks]));
+      pacc = Op::mfma(a2, b2, pacc);                   // dP = dO V^T
+    }
+    // masked scores -> -inf (P = 0, dS = 0) on blocks that straddle the
+    // diagonal or the end of the sequence
+    if ((q0 + 32 > N) || (CAUSAL && q0 < wk0 + 31)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = q0 + key_of_reg(i, g);
+        if ((qi >= N) || (CAUSAL && key > qi)) sacc[i] = -INFINITY;
+      }
+    }
+    // register i holds query q0 + 16 (i >> 3) + 8 g + (i & 7); its LSE and D
+    const float* sl = sts + qh * 32 + 8 * g;
+    frag pf[2], dsf[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const f32x4_t l0 = *(const f32x4_t*)(sl + 16 * cc);
+      const f32x4_t l1 = *(const f32x4_t*)(sl + 16 * cc + 4);
+      const f32x4_t d0 = *(const f32x4_t*)(sl + BN + 16 * cc);
+      const f32x4_t d1 = *(const f32x4_t*)(sl + BN + 16 * cc + 4);
+      u32x4_t wp, wd;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float pr2[2], ds2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = 2 * t + u;           // 0..7 within the chunk
+          const float lse = e < 4 ? l0[e] : l1[e - 4];
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          const int i = cc * 8 + e;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lse * kLog2e));
+          pr2[u] = pr;
+          ds2[u] = pr * (pacc[i] - dl);
+        }
+        wp[t] = Op::pack2(pr2[0], pr2[1]);
+        wd[t] = Op::pack2(ds2[0], ds2[1]);
+      }
+      pf[cc] = __builtin_bit_cast(frag, wp);
+      dsf[cc] = __builtin_bit_cast(frag, wd);
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        dvacc[db] = Op::mfma(read_tr<frag, D>(orows + cc * 16 * RB, ta, db), pf[cc], dvacc[db]);
+        dkacc[db] = Op::mfma(read_tr<frag, D>(qrows + cc * 16 * RB, ta, db), dsf[cc], dkacc[db]);
+      }
+  };
+
+  auto copy = [&](int tile, int st) __attribute__((always_inline)) {
+    int off[LOADS];
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) off[t] = dma_off[t] + tile * BN * RB;
+    dma_tile<LOADS, NT>(qrs, st ? sq1 : sq0, wave, 0, off);
+    dma_tile<LOADS, NT>(ors, st ? so1 : so0, wave, 0, off);
+    float* sts = st ? st1 : st0;
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void_t*)sts, 4, (tile * BN + lane) * 4, 0, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void_t*)(sts + BN), 4, (tile * BN + lane) * 4, 0, 0, 0);
+  };
+  // every wave runs every tile (wholly masked blocks add zero; waves past N
+  // are never stored) -- no per-wave control flow around the accumulators
+  auto step = [&](int j, int st) __attribute__((always_inline)) {
+    if (j + 1 < n_qt) copy(j + 1, st ^ 1);
+    block(j * BN + qh * 32, st ? sq1 : sq0, st ? so1 : so0, st ? st1 : st0);
+    wait_vmem();
+    __syncthreads();
+  };
+  if (qt_begin < n_qt) copy(qt_begin, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = qt_begin; j < n_qt; j += 2) {
+    step(j, 0);
+    if (j + 1 < n_qt) step(j + 1, 1);
+  }
+
+  // pair exchange: waves 4..7 park their dK partial in skv, waves 0..3 their
+  // dV partial in the tile buffers (slot = key group); layout [register][lane]
+  {
+    char* slot_kv = skv + kg * XCH;
+    char* slot_t = kg == 0 ? sq0 : kg == 1 ? sq1 : kg == 2 ? so0 : so1;
+    float* dst = (float*)(qh ? slot_kv : slot_t);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = qh ? dkacc[db][i] : dvacc[db][i];
+    __syncthreads();
+    const float* src = (const float*)(qh ? slot_t : slot_kv);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float o = src[(db * 16 + i) * 64 + lane];
+        if (qh) dvacc[db][i] += o;
+        else dkacc[db][i] += o;
+      }
+  }
+  if (key < N) {
+    const int64_t row_off = (head + key) * RB;
+    if (qh) store_rowT<T, D>(p.dv + row_off, dvacc, 1.f, g);
+    else store_rowT<T, D>(p.dk + row_off, dkacc, p.scale, g);
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   BwdParams p;
@@ -521,7 +748,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((attn_bwd_dkdv8_kernel<T, D, CAUSAL>), dim3(p.total), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 
