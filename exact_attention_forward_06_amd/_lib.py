@@ -84,6 +84,25 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _buf(t, shape, dtype, device, name):
+    """An output or workspace tensor: allocated when t is None, else checked
+    to be contiguous with exactly the shape, dtype and device the kernels
+    will write (the C ABI cannot see a tensor's size)."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous() or t.device != torch.device(device):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {device}; got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    return t
+
+
+def _check_signs(signs, d):
+    if signs is not None and (signs.dtype != torch.int8 or tuple(signs.shape) != (d,) or not signs.is_contiguous()):
+        raise ValueError(f"signs must be a contiguous int8 vector of length d = {d}")
+
+
 def _bhnd_strides(*ts):
     s = ts[0].stride()
     for t in ts:
@@ -104,10 +123,9 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, retu
         raise ValueError("q, k, v must share one dtype among fp32, fp16, bf16")
     B, H, N, d = q.shape
     strides = _bhnd_strides(q, k, v)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = _buf(out, (B, H, N, d), q.dtype, q.device, "out")
+    if lse is not None or return_lse:
+        lse = _buf(lse, (B, H, N), torch.float32, q.device, "lse")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides,
                         _ptr(out), _ptr(lse), scale, int(bool(causal)), _stream(stream)))
@@ -132,14 +150,10 @@ def attn_fwd_splitkv(q, k, v, num_splits, causal=False, softmax_scale=None, out=
     B, H, N, d = q.shape
     strides = _bhnd_strides(q, k, v)
     dev = q.device
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=q.dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    if o_part is None:
-        o_part = torch.empty((num_splits, B, H, N, d), dtype=torch.float32, device=dev)
-    if lse_part is None:
-        lse_part = torch.empty((num_splits, B, H, N), dtype=torch.float32, device=dev)
+    out = _buf(out, (B, H, N, d), q.dtype, dev, "out")
+    lse = _buf(lse, (B, H, N), torch.float32, dev, "lse")
+    o_part = _buf(o_part, (num_splits, B, H, N, d), torch.float32, dev, "o_part")
+    lse_part = _buf(lse_part, (num_splits, B, H, N), torch.float32, dev, "lse_part")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd_splitkv(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides,
                                 int(num_splits), _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
@@ -158,10 +172,8 @@ def attn_merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None, s
     S, B, H, N, d = o_part.shape
     if tuple(lse_part.shape) != (S, B, H, N):
         raise ValueError("lse_part must be [S, B, H, N]")
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=out_dtype, device=o_part.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+    out = _buf(out, (B, H, N, d), out_dtype if out is None else out.dtype, o_part.device, "out")
+    lse = _buf(lse, (B, H, N), torch.float32, o_part.device, "lse")
     _check(lib.attn_merge(_DTYPE_CODE[out.dtype], S, B, H, N, d, _ptr(o_part), _ptr(lse_part), _ptr(out),
                           _ptr(lse), _stream(stream)))
     return out, lse
@@ -179,13 +191,9 @@ def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, ou
     B, H, N, d = x.shape
     strides = _bhnd_strides(x)
     nblk = -(-N // block_rows)
-    if out is None:
-        shape = (B, H, d, N) if transpose_out else (B, H, N, d)
-        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
-    if signs is not None and signs.dtype != torch.int8:
-        raise ValueError("signs must be int8")
+    out = _buf(out, (B, H, d, N) if transpose_out else (B, H, N, d), torch.uint8, x.device, "out")
+    scales = _buf(scales, (B, H, nblk), torch.float32, x.device, "scales")
+    _check_signs(signs, d)
     _check(lib.hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides,
                                      _ptr(signs), block_rows, FP8_FORMATS[fp8_format],
                                      int(bool(transpose_out)), _ptr(out), _ptr(scales), _stream(stream)))
@@ -208,12 +216,9 @@ def rope_hadamard_rotate_quant(x, signs=None, style="interleaved", base=10000.0,
     B, H, N, d = x.shape
     strides = _bhnd_strides(x)
     nblk = -(-N // block_rows)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
-    if signs is not None and signs.dtype != torch.int8:
-        raise ValueError("signs must be int8")
+    out = _buf(out, (B, H, N, d), torch.uint8, x.device, "out")
+    scales = _buf(scales, (B, H, nblk), torch.float32, x.device, "scales")
+    _check_signs(signs, d)
     _check(lib.rope_hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides, ROPE_STYLES[style],
                                           float(base), int(pos_offset), _ptr(signs), block_rows,
                                           FP8_FORMATS[fp8_format], _ptr(out), _ptr(scales), _stream(stream)))
@@ -229,10 +234,17 @@ def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False, softmax_s
     for t in (q8, k8, v8t, q_scale, k_scale, v_scale):
         if not t.is_contiguous():
             raise ValueError("attn_fwd_fp8 takes contiguous tensors")
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    nblk = -(-N // block_rows)
+    for name, t, shape, dt in (("q8", q8, (B, H, N, d), torch.uint8), ("k8", k8, (B, H, N, d), torch.uint8),
+                               ("v8t", v8t, (B, H, d, N), torch.uint8),
+                               ("q_scale", q_scale, (B, H, nblk), torch.float32),
+                               ("k_scale", k_scale, (B, H, nblk), torch.float32),
+                               ("v_scale", v_scale, (B, H, nblk), torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"{name} must be {dt} of shape {shape}; got {t.dtype} {tuple(t.shape)}")
+    out = _buf(out, (B, H, N, d), torch.bfloat16, q8.device, "out")
+    if lse is not None or return_lse:
+        lse = _buf(lse, (B, H, N), torch.float32, q8.device, "lse")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd_fp8(B, H, N, d, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
                             _ptr(v8t), _ptr(v_scale), block_rows, FP8_FORMATS[fp8_format], _ptr(out),
@@ -262,11 +274,10 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, dq=None, d
     if tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be [B, H, N]")
     dev = q.device
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq = _buf(dq, (B, H, N, d), q.dtype, dev, "dq")
+    dk = _buf(dk, (B, H, N, d), q.dtype, dev, "dk")
+    dv = _buf(dv, (B, H, N, d), q.dtype, dev, "dv")
+    delta = _buf(delta, (B, H, N), torch.float32, dev, "delta")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_bwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                         _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)),
