@@ -132,7 +132,7 @@ def test_bwd_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("workload", ["bf16_n2048", "bf16_causal_8k"])
+@pytest.mark.parametrize("workload", ["bf16_n2048", "bf16_causal_8k", "bf16_d64"])
 def test_bwd_full_size(workload):
     """The forward workloads' full shapes: the GPU forward feeds the backward;
     two heads (the first and the last) are compared with the oracle whole,
