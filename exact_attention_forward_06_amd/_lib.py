@@ -37,8 +37,8 @@ _SIGNATURES = {
     "attn_merge": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
     "rope_hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.c_double, _i, _vp, _i, _i, _vp,
                                     _vp, _vp], _i),
-    "attn_bwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
-                  _i, _vp], _i),
+    "attn_bwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                  ctypes.c_float, _i, _vp], _i),
 }
 
 _lib = None
@@ -256,17 +256,19 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, dq=None, d
              delta=None, stream=None):
     """Gradients (dq, dk, dv) of attn_fwd for the upstream gradient dout,
     from the forward's inputs and outputs (o, lse) -- fp16 / bf16, d = 64 or
-    128, contiguous [B, H, N, d] tensors.  `delta` (fp32 [B, H, N]) is the
-    library's workspace, allocated unless given; on return it holds
-    dO_i . O_i.  Returns (dq, dk, dv, delta)."""
+    128.  q, k, v are [B, H, N, d] with a contiguous last dim and shared
+    strides (as in attn_fwd); o, dout and the gradients are contiguous.
+    `delta` (fp32 [B, H, N]) is the library's workspace, allocated unless
+    given; on return it holds dO_i . O_i.  Returns (dq, dk, dv, delta)."""
     lib = load()
     if q.dtype not in _DTYPE_CODE or any(t.dtype != q.dtype for t in (k, v, o, dout)):
         raise ValueError("q, k, v, o, dout must share a dtype among fp16, bf16")
     if lse.dtype != torch.float32:
         raise ValueError("lse must be fp32")
-    for t in (q, k, v, o, dout, lse):
+    for t in (o, dout, lse):
         if not t.is_contiguous():
-            raise ValueError("attn_bwd takes contiguous tensors")
+            raise ValueError("attn_bwd takes contiguous o, dout and lse")
+    strides = _bhnd_strides(q, k, v)
     B, H, N, d = q.shape
     for t in (k, v, o, dout):
         if t.shape != q.shape:
@@ -274,12 +276,12 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, dq=None, d
     if tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be [B, H, N]")
     dev = q.device
-    dq = _buf(dq, (B, H, N, d), q.dtype, dev, "dq")
+    dq = _buf(dq, (B, H, N, d), q.dtype, dev, "dq")     # gradients are contiguous
     dk = _buf(dk, (B, H, N, d), q.dtype, dev, "dk")
     dv = _buf(dv, (B, H, N, d), q.dtype, dev, "dv")
     delta = _buf(delta, (B, H, N), torch.float32, dev, "delta")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    _check(lib.attn_bwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+    _check(lib.attn_bwd(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides, _ptr(o), _ptr(lse),
                         _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)),
                         _stream(stream)))
     return dq, dk, dv, delta

@@ -455,9 +455,9 @@ int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_s
 }  // extern "C"
 
 extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, const void* k,
-                        const void* v, const void* o, const float* lse, const void* dout,
-                        float* delta, void* dq, void* dk, void* dv, float softmax_scale,
-                        int causal, void* stream) {
+                        const void* v, const int64_t* qkv_strides, const void* o, const float* lse,
+                        const void* dout, float* delta, void* dq, void* dk, void* dv,
+                        float softmax_scale, int causal, void* stream) {
   const int es = elem_size(dtype);
   if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (int st = check_sizes(B, H, N, d)) return st;
@@ -466,10 +466,12 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
     return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd covers fp16 / bf16 with d = 64 or 128");
   const int64_t rows = (int64_t)B * H * N;
   const int64_t tbytes = rows * d * es;
+  int64_t sb, sh, sn;
+  strides_or_contiguous(qkv_strides, H, N, d, &sb, &sh, &sn);
   Span sq, sk, sv, so, sl, sdo, sdl, sdq, sdk, sdv;
-  if (int st = check_dense("q", q, tbytes, &sq)) return st;
-  if (int st = check_dense("k", k, tbytes, &sk)) return st;
-  if (int st = check_dense("v", v, tbytes, &sv)) return st;
+  if (int st = check_strided("q", q, B, H, N, d, sb, sh, sn, es, &sq)) return st;
+  if (int st = check_strided("k", k, B, H, N, d, sb, sh, sn, es, &sk)) return st;
+  if (int st = check_strided("v", v, B, H, N, d, sb, sh, sn, es, &sv)) return st;
   if (int st = check_dense("o", o, tbytes, &so)) return st;
   if (int st = check_dense("lse", lse, rows * 4, &sl, false)) return st;
   if (int st = check_dense("dout", dout, tbytes, &sdo)) return st;
@@ -487,7 +489,7 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
   }
   // one head's rows are addressed with 32-bit buffer offsets (including up
   // to one 128-row block past N, which reads as zero)
-  if (((int64_t)N + 128) * d * es >= ((int64_t)1 << 31))
+  if (((int64_t)N + 128) * (sn > d ? sn : d) * es + (int64_t)d * es >= ((int64_t)1 << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
 
   attn::BwdArgs a;
@@ -499,6 +501,9 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
   a.q = q;
   a.k = k;
   a.v = v;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
   a.o = o;
   a.dout = dout;
   a.lse = lse;

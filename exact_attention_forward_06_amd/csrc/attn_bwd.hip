@@ -64,7 +64,8 @@ struct BwdParams {
   char* dq;
   char* dk;
   char* dv;
-  int N, nblk, total;
+  int64_t sb, sh, sn;    // element strides (b, h, n) of q, k and v; the rest is contiguous
+  int H, N, nblk, total;
   float scale;           // softmax scale
   float scale_log2;      // softmax scale * log2(e)
 };
@@ -202,10 +203,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int q_row = wq0 + n;
   const bool q_ok = q_row < N;
   const int64_t head = (int64_t)bh * N;      // row index of the head's first row
-  const int64_t row_off = (head + q_row) * RB;
+  const int64_t row_off = (head + q_row) * RB;   // contiguous tensors (o, dout, dq)
+  const int bb = bh / p.H;
+  const int64_t qkv_off = (bb * p.sb + (int64_t)(bh - bb * p.H) * p.sh) * 2;   // strided q, k, v
+  const int rbg = (int)(p.sn * 2);                                                // their row pitch
 
   frag qf[NKS], dof[NKS];
-  load_row_frags<T, D>(qf, p.q + row_off, q_ok, g);
+  load_row_frags<T, D>(qf, p.q + qkv_off + (int64_t)q_row * rbg, q_ok, g);
   load_row_frags<T, D>(dof, p.dout + row_off, q_ok, g);
 
   // D_i = dO_i . O_i (fp32 products of the 16-bit values), stored for dkdv
@@ -225,19 +229,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
   }
   const float lse2 = q_ok ? p.lse[head + q_row] * kLog2e : 0.f;
 
-  const int64_t extent = (int64_t)N * RB;
+  const int64_t extent = ((int64_t)(N - 1) * p.sn + D) * 2;
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * RB), (short)0, (int)extent, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qkv_off), (short)0, (int)extent, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head * RB), (short)0, (int)extent, 0x00020000);
-  int dma_off[LOADS];
-#pragma unroll
-  for (int t = 0; t < LOADS; ++t) {
-    const int pos = (t * NT + tid) * 16;
-    const int row = pos / RB;
-    const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
-    dma_off[t] = row * RB + chunk * 16;
-  }
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + qkv_off), (short)0, (int)extent, 0x00020000);
   const TileAddr<D> ta(lane);
 
   f32x16_t dqacc[NDB];
@@ -292,12 +288,19 @@ void attn_bwd_dq_kernel(BwdParams p) {
         dqacc[db] = Op::mfma(read_tr<frag, D>(kt + cc * 16 * RB, ta, db), dsf[cc], dqacc[db]);
   };
 
-  // the tile offset goes into the per-lane offset, which the buffer range
-  // check always covers: rows past N read as zero
+  // The tile offset goes into the per-lane offset, which the buffer range
+  // check always covers: rows past N read as zero.  DMA instruction t of a
+  // lane covers row t * RPT + lane_row of the tile; RPT is a multiple of 16,
+  // so the swizzled chunk depends on the lane alone and the offsets differ by
+  // a wave-uniform term (one live register: this kernel is at its limit).
+  constexpr int RPT = NT * 16 / RB;
+  static_assert(RPT % 16 == 0, "swizzle period");
+  const int lane_row = tid * 16 / RB;
+  const int lane_off = lane_row * rbg + ((((tid * 16) % RB) / 16) ^ swz<D>(lane_row)) * 16;
   auto copy = [&](int tile, int st) __attribute__((always_inline)) {
     int off[LOADS];
 #pragma unroll
-    for (int t = 0; t < LOADS; ++t) off[t] = dma_off[t] + tile * BN * RB;
+    for (int t = 0; t < LOADS; ++t) off[t] = lane_off + (tile * BN + t * RPT) * rbg;
     dma_tile<LOADS, NT>(krs, st ? sk1 : sk0, wave, 0, off);
     dma_tile<LOADS, NT>(vrs, st ? sv1 : sv0, wave, 0, off);
   };
@@ -360,28 +363,31 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int key = wk0 + n;
   const bool k_ok = key < N;
   const int64_t head = (int64_t)bh * N;
-  const int64_t row_off = (head + key) * RB;
+  const int64_t row_off = (head + key) * RB;     // contiguous tensors (dout, dk, dv)
+  const int bb = bh / p.H;
+  const int64_t qkv_off = (bb * p.sb + (int64_t)(bh - bb * p.H) * p.sh) * 2;   // strided q, k, v
+  const int rbg = (int)(p.sn * 2);
 
   frag kf[NKS], vf[NKS];
-  load_row_frags<T, D>(kf, p.k + row_off, k_ok, g);
-  load_row_frags<T, D>(vf, p.v + row_off, k_ok, g);
+  load_row_frags<T, D>(kf, p.k + qkv_off + (int64_t)key * rbg, k_ok, g);
+  load_row_frags<T, D>(vf, p.v + qkv_off + (int64_t)key * rbg, k_ok, g);
 
-  const int64_t extent = (int64_t)N * RB;
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + head * RB), (short)0, (int)extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.q + qkv_off), (short)0, (int)(((int64_t)(N - 1) * p.sn + D) * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t ors =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * RB), (short)0, (int)extent, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * RB), (short)0, (int)((int64_t)N * RB), 0x00020000);
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + head), (short)0, N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t drs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + head), (short)0, N * 4, 0x00020000);
-  int dma_off[LOADS];
+  int dma_q[LOADS], dma_o[LOADS];   // Q rows at the strided pitch, dO rows contiguous
 #pragma unroll
   for (int t = 0; t < LOADS; ++t) {
     const int pos = (t * NT + tid) * 16;
     const int row = pos / RB;
     const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
-    dma_off[t] = row * RB + chunk * 16;
+    dma_q[t] = row * rbg + chunk * 16;
+    dma_o[t] = row * RB + chunk * 16;
   }
   const TileAddr<D> ta(lane);
 
@@ -463,11 +469,14 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   // tile offsets go into the per-lane offsets, which the buffer range check
   // always covers: rows (and LSE / D entries) past N read as zero
   auto copy = [&](int tile, int st) __attribute__((always_inline)) {
-    int off[LOADS];
+    int offq[LOADS], offo[LOADS];
 #pragma unroll
-    for (int t = 0; t < LOADS; ++t) off[t] = dma_off[t] + tile * BN * RB;
-    dma_tile<LOADS, NT>(qrs, st ? sq1 : sq0, wave, 0, off);
-    dma_tile<LOADS, NT>(ors, st ? so1 : so0, wave, 0, off);
+    for (int t = 0; t < LOADS; ++t) {
+      offq[t] = dma_q[t] + tile * BN * rbg;
+      offo[t] = dma_o[t] + tile * BN * RB;
+    }
+    dma_tile<LOADS, NT>(qrs, st ? sq1 : sq0, wave, 0, offq);
+    dma_tile<LOADS, NT>(ors, st ? so1 : so0, wave, 0, offo);
     // the tile's LSE (wave 0) and D (wave 1): 64 floats, one per lane
     float* sts = st ? st1 : st0;
     if (wave == 0)
@@ -548,16 +557,19 @@ void attn_bwd_dkdv8_kernel(BwdParams p) {
   const int wk0 = k0 + kg * 32;
   const int key = wk0 + n;
   const int64_t head = (int64_t)bh * N;
+  const int bb = bh / p.H;
+  const int64_t qkv_off = (bb * p.sb + (int64_t)(bh - bb * p.H) * p.sh) * 2;   // strided q, k, v
+  const int rbg = (int)(p.sn * 2);
 
-  const int64_t extent = (int64_t)N * RB;
+  const int ext_qkv = (int)(((int64_t)(N - 1) * p.sn + D) * 2);
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * RB), (short)0, (int)extent, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qkv_off), (short)0, ext_qkv, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head * RB), (short)0, (int)extent, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + qkv_off), (short)0, ext_qkv, 0x00020000);
   const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + head * RB), (short)0, (int)extent, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qkv_off), (short)0, ext_qkv, 0x00020000);
   const __amdgpu_buffer_rsrc_t ors =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * RB), (short)0, (int)extent, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * RB), (short)0, (int)((int64_t)N * RB), 0x00020000);
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + head), (short)0, N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t drs =
@@ -570,17 +582,19 @@ void attn_bwd_dkdv8_kernel(BwdParams p) {
     for (int t = 0; t < KV_LOADS; ++t) {
       const int pos = (t * NT + tid) * 16;
       const int row = pos / RB;
-      off[t] = (k0 + row) * RB + (((pos % RB) / 16) ^ swz<D>(row)) * 16;
+      off[t] = (k0 + row) * rbg + (((pos % RB) / 16) ^ swz<D>(row)) * 16;
     }
     dma_tile<KV_LOADS, NT>(krs, skv, wave, 0, off);
     dma_tile<KV_LOADS, NT>(vrs, skv + KVB, wave, 0, off);
   }
-  int dma_off[LOADS];
+  int dma_q[LOADS], dma_o[LOADS];   // Q rows at the strided pitch, dO rows contiguous
 #pragma unroll
   for (int t = 0; t < LOADS; ++t) {
     const int pos = (t * NT + tid) * 16;
     const int row = pos / RB;
-    dma_off[t] = row * RB + (((pos % RB) / 16) ^ swz<D>(row)) * 16;
+    const int chunk = (((pos % RB) / 16) ^ swz<D>(row)) * 16;
+    dma_q[t] = row * rbg + chunk;
+    dma_o[t] = row * RB + chunk;
   }
   const TileAddr<D> ta(lane);
   // B operand rows of K and V: lane (n, g) reads chunk 2 ks + g of key row kg * 32 + n
@@ -672,11 +686,14 @@ void attn_bwd_dkdv8_kernel(BwdParams p) {
   };
 
   auto copy = [&](int tile, int st) __attribute__((always_inline)) {
-    int off[LOADS];
+    int offq[LOADS], offo[LOADS];
 #pragma unroll
-    for (int t = 0; t < LOADS; ++t) off[t] = dma_off[t] + tile * BN * RB;
-    dma_tile<LOADS, NT>(qrs, st ? sq1 : sq0, wave, 0, off);
-    dma_tile<LOADS, NT>(ors, st ? so1 : so0, wave, 0, off);
+    for (int t = 0; t < LOADS; ++t) {
+      offq[t] = dma_q[t] + tile * BN * rbg;
+      offo[t] = dma_o[t] + tile * BN * RB;
+    }
+    dma_tile<LOADS, NT>(qrs, st ? sq1 : sq0, wave, 0, offq);
+    dma_tile<LOADS, NT>(ors, st ? so1 : so0, wave, 0, offo);
     float* sts = st ? st1 : st0;
     if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void_t*)sts, 4, (tile * BN + lane) * 4, 0, 0, 0);
@@ -740,6 +757,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.dq = static_cast<char*>(a.dq);
   p.dk = static_cast<char*>(a.dk);
   p.dv = static_cast<char*>(a.dv);
+  p.sb = a.sb;
+  p.sh = a.sh;
+  p.sn = a.sn;
+  p.H = a.H;
   p.N = a.N;
   p.nblk = (a.N + kBwdBlock - 1) / kBwdBlock;
   p.total = a.B * a.H * p.nblk;

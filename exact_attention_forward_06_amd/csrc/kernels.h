@@ -71,10 +71,11 @@ struct Fp8FwdArgs {
 struct BwdArgs {
   Dtype dtype;          // F16 or BF16
   int B, H, N, d;
-  const void* q;        // contiguous [B, H, N, d]
+  const void* q;        // [B, H, N, d], element strides sb, sh, sn (d stride 1)
   const void* k;
   const void* v;
-  const void* o;        // forward output
+  int64_t sb, sh, sn;
+  const void* o;        // forward output, contiguous
   const void* dout;     // upstream gradient dO
   const float* lse;     // forward LSE [B, H, N]
   float* delta;         // workspace [B, H, N]: dO . O per row

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum {
@@ -289,7 +289,9 @@ int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  *   dtype          ATTN_F16 or ATTN_BF16 (ATTN_F32: ATTN_ERR_UNSUPPORTED):
  *                  type of q, k, v, o, dout, dq, dk, dv.
  *   B, H, N, d     as in attn_fwd; d in {64, 128} (256: ATTN_ERR_UNSUPPORTED).
- *   q, k, v        device [B, H, N, d] forward inputs, contiguous.
+ *   q, k, v        device [B, H, N, d] forward inputs.
+ *   qkv_strides    host array of 3 int64 element strides (b, h, n) shared by
+ *                  q, k and v, as in attn_fwd; NULL = contiguous.
  *   o, lse         device forward outputs of attn_fwd on the same q, k, v,
  *                  softmax_scale and causal: o [B, H, N, d] contiguous,
  *                  lse fp32 [B, H, N].
@@ -308,6 +310,7 @@ int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  */
 int attn_bwd(int dtype, int B, int H, int N, int d,
              const void* q, const void* k, const void* v,
+             const int64_t* qkv_strides,
              const void* o, const float* lse, const void* dout,
              float* delta, void* dq, void* dk, void* dv,
              float softmax_scale, int causal, void* stream);

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
                           "attn_bwd", "rope_hadamard_rotate_quant"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -182,9 +182,10 @@ BW = {name: 0x100000000 + i * 0x10000000 for i, name in
       enumerate(("q", "k", "v", "o", "lse", "dout", "delta", "dq", "dk", "dv"))}
 
 
-def _bwd(lib, dtype=2, B=1, H=2, N=100, d=128, scale=0.125, causal=0, **ptrs):
+def _bwd(lib, dtype=2, B=1, H=2, N=100, d=128, scale=0.125, causal=0, strides=None, **ptrs):
     p = dict(BW, **ptrs)
-    return lib.attn_bwd(dtype, B, H, N, d, p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["delta"],
+    st = None if strides is None else (ctypes.c_int64 * 3)(*strides)
+    return lib.attn_bwd(dtype, B, H, N, d, p["q"], p["k"], p["v"], st, p["o"], p["lse"], p["dout"], p["delta"],
                         p["dq"], p["dk"], p["dv"], scale, causal, None)
 
 
@@ -207,6 +208,9 @@ def _bwd(lib, dtype=2, B=1, H=2, N=100, d=128, scale=0.125, causal=0, **ptrs):
     (dict(delta=BW["lse"]), 1, "overlaps an input"),
     (dict(dk=BW["dq"] + 0x200), 1, "outputs overlap"),
     (dict(delta=BW["dv"] + 0x40), 1, "outputs overlap"),
+    (dict(strides=(2 * 100 * 128, 100 * 128, 64)), 1, "rows overlap"),
+    (dict(strides=(2 * 100 * 136, 100 * 136, 132)), 1, "multiples of 16 bytes"),
+    (dict(strides=(-1, 100 * 128, 128)), 1, "negative stride"),
 ])
 def test_bwd_rejects(lib, kw, status, msg):
     assert _bwd(lib, **kw) == status

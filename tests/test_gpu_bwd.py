@@ -119,6 +119,27 @@ def test_bwd_softmax_scale():
     _check(dv, dv_r, "dV")
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_strided_qkv(causal, d):
+    """q, k, v as views of one packed [B, N, 3, H, d] projection (strides
+    (N*3*H*d, d, 3*H*d)), the layout attn_fwd also accepts; o, dout and the
+    gradients contiguous."""
+    B, H, N = 2, 3, 333
+    print(f"attn_bwd strided q/k/v d={d} causal={causal}", flush=True)
+    inp, do, s, x64 = _case(B, H, N, d, torch.bfloat16, causal, seed=17 + d)
+    packed = torch.stack([inp[n].permute(0, 2, 1, 3) for n in ("q", "k", "v")], dim=2).contiguous().cuda()
+    q, k, v = (packed[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    assert not q.is_contiguous() and q.stride() == (N * 3 * H * d, d, 3 * H * d, 1)
+    o, lse = attn_fwd(q, k, v, causal=causal)
+    dq, dk, dv, _ = attn_bwd(q, k, v, o, lse, do.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = oracle.attention_backward(*x64, s, causal)
+    _check(dq, dq_r, "dQ")
+    _check(dk, dk_r, "dK")
+    _check(dv, dv_r, "dV")
+
+
 def test_bwd_deterministic():
     """No atomics: two calls give bitwise identical gradients."""
     B, H, N, d = 2, 4, 777, 128
