@@ -19,9 +19,9 @@ Sources and readings:
   * Per-block quantisation with one scale per block: the "FlashAttention-2/3"
     page, 特性三 (block-level online quantisation).  Readings: a block is
     128 consecutive rows of one (b, h) over all d columns; the stored
-    dequantisation scale is s = amax / 448 (amax = 0 gives s = 1 and all
-    codes zero); code = E4M3 round-to-nearest-even of x * 448 / amax,
-    saturating at +-448.
+    dequantisation scale is s = amax / 448 (so an all-zero block has s = 0
+    and all codes zero: it dequantises to zero exactly); code = E4M3
+    round-to-nearest-even of x * 448 / amax, saturating at +-448.
   * E4M3 itself: the FP8 formats named on the "FlashAttention-2/3" page
     (特性二).  The codec below is the OCP "E4M3FN" encoding, written from
     its definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
@@ -173,7 +173,7 @@ def block_quantize(x, block_rows=128, fmt="e4m3"):
         yb = np.where((amax > 0)[..., None, None], (blk * qmax) / safe[..., None, None], 0.0)
         y[..., r0:r1, :] = yb
         codes[..., r0:r1, :] = encode(yb)
-        scales[..., b] = np.where(amax > 0, amax / qmax, 1.0)
+        scales[..., b] = amax / qmax
     return codes, scales, y
 
 
@@ -199,39 +199,74 @@ def dequantize(codes, scales, block_rows=128, transposed=False, fmt="e4m3"):
 
 
 def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
-                            quantize_p=False, p_gain=256.0, fmt="e4m3"):
-    """Step-by-step simulation of FP8 attention (diagnostic floor).
+                            quantize_p=False, fmt="e4m3"):
+    """Step-by-step simulation of FP8 attention.
 
     1. Rotate Q and K with the shared signs (skipped if signs is None).
     2. Block-quantise Q~, K~ and V and dequantise them.
-    3. Evaluate the exact definition on the dequantised values.  With
-       quantize_p, P is additionally rounded as E4M3(P * p_gain) / p_gain
-       and the rounded P serves both the product with V and the row sums
-       (the reading in which O is normalised by the weights it used; the
-       pages leave the precision of P's second product open).
+    3. Evaluate the exact definition on the dequantised values.
+
+    With quantize_p the probabilities of the second product are rounded to
+    E4M3 as well (the pages put both products on the FP8 path but leave the
+    rounding of P open).  Reading, per head and query row i:
+      * t_ij = s_ij log2(e) (scores in log2 units, masked ones -inf) and
+        M_i = ceil(max_j t_ij): the row's reference is a power of two, so the
+        rounding grid of the weights does not depend on where exactly the
+        maximum lies;
+      * V's block scale is folded into the weight before rounding: with
+        w_j the scale of key j's V block (the largest V block scale of the
+        head, svmax, for an all-zero block, whose codes contribute nothing)
+        and gain g_j = 16 w_j / svmax,
+            P'_ij = E4M3(2^(t_ij - M_i) g_j),   P~_ij = P'_ij / g_j;
+      * the rounded weights serve both the product with V and the row sums:
+            l_i = sum_j P~_ij,  O_i = sum_j P~_ij V^_j / l_i,
+            LSE_i = M_i ln 2 + ln l_i,
+        so O is normalised by exactly the weights it used (a constant V comes
+        out unchanged).
     Returns fp64 (O, LSE).
     """
-    qh = dequantize(*hadamard_rotate_quant(q, signs, block_rows, fmt=fmt)[:2], block_rows, fmt=fmt)
-    kh = dequantize(*hadamard_rotate_quant(k, signs, block_rows, fmt=fmt)[:2], block_rows, fmt=fmt)
-    vh = dequantize(*hadamard_rotate_quant(v, None, block_rows, fmt=fmt)[:2], block_rows, fmt=fmt)
+    qc, qs, _ = hadamard_rotate_quant(q, signs, block_rows, fmt=fmt)
+    kc, ks, _ = hadamard_rotate_quant(k, signs, block_rows, fmt=fmt)
+    vc, vs, _ = hadamard_rotate_quant(v, None, block_rows, fmt=fmt)
+    qh = dequantize(qc, qs, block_rows, fmt=fmt)
+    kh = dequantize(kc, ks, block_rows, fmt=fmt)
+    vh = dequantize(vc, vs, block_rows, fmt=fmt)
     if not quantize_p:
         return _attention_exact(qh, kh, vh, scale, causal)
     lead = qh.shape[:-2]
     n, d = qh.shape[-2:]
     qf, kf, vf = (a.reshape(-1, a.shape[-2], a.shape[-1]) for a in (qh, kh, vh))
+    vsf = np.asarray(vs, np.float64).reshape(qf.shape[0], -1)
     o = np.empty((qf.shape[0], n, vf.shape[-1]))
     lse = np.empty((qf.shape[0], n))
     for h in range(qf.shape[0]):
         s = (qf[h] @ kf[h].T) * scale
         if causal:
             s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
-        m = s.max(1)
-        e = np.exp(s - m[:, None])
-        eq = e4m3_decode(e4m3_encode(e * p_gain)) / p_gain
-        l = eq.sum(1)
-        o[h] = (eq @ vf[h]) / l[:, None]
-        lse[h] = m + np.log(l)
+        w = np.repeat(vsf[h], block_rows)[:n]
+        pq, m = quantized_probabilities(s, w)
+        l = pq.sum(1)
+        o[h] = (pq @ vf[h]) / l[:, None]
+        lse[h] = m * np.log(2.0) + np.log(l)
     return o.reshape(*lead, n, -1), lse.reshape(*lead, n)
+
+
+def quantized_probabilities(s, w):
+    """The E4M3-rounded weights of the FP8 second product (the reading stated
+    in attention_fp8_simulated).  s: scores [Nq, Nk] in natural units
+    (masked entries -inf); w: [Nk] the V block scale of each key.  Returns
+    (P~ [Nq, Nk], M [Nq]) with M_i = ceil(max_j s_ij log2 e) and
+    P~_ij = E4M3(2^(s_ij log2 e - M_i) g_j) / g_j, g_j = 16 w_j / svmax
+    (w_j = svmax for a zero scale; svmax = 1 if every scale is zero)."""
+    s = np.asarray(s, np.float64)
+    w = np.asarray(w, np.float64)
+    t = s * np.log2(np.e)
+    m = np.ceil(np.max(t, axis=1))
+    svmax = float(np.max(w)) if np.max(w) > 0 else 1.0
+    w = np.where(w > 0, w, svmax)
+    gain = 16.0 * w / svmax
+    pq = e4m3_decode(e4m3_encode(np.exp2(t - m[:, None]) * gain[None, :])) / gain[None, :]
+    return pq, m
 
 
 def rel_rms(a, b):

@@ -241,12 +241,14 @@ def test_exact_rounding_ties_resolve_to_even():
     assert codes[0, 0, 0, 0] == 0x7E and codes[1, 0, 0, 0] == 0x7E
 
 
-def test_zero_block_gets_unit_scale():
+def test_zero_block_gets_zero_scale():
+    # s = amax / 448 with amax = 0: the block dequantises to exact zeros
     x = np.zeros((1, 1, 256, 8))
     x[0, 0, 200, 3] = -2.5
     codes, scales, _ = block_quantize(x, 128)
-    assert scales[0, 0, 0] == 1.0 and np.all(e4m3_decode(codes[0, 0, :128]) == 0)
+    assert scales[0, 0, 0] == 0.0 and np.all(e4m3_decode(codes[0, 0, :128]) == 0)
     assert scales[0, 0, 1] == 2.5 / 448
+    np.testing.assert_array_equal(dequantize(codes, scales, 128), x)
 
 
 def _grid_exact(shape, seed, block_rows=128):
@@ -302,8 +304,8 @@ def test_fp8_simulation_error_is_small_but_nonzero():
     o_p, lse_p = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, quantize_p=True)
     assert 0 < oracle.rel_rms(o_p, o_sim) < 0.06
     # rounded P in the row sums: l moves by at most the E4M3 relative rounding
-    # (2^-4 for values in the normal range, which p_gain = 256 keeps the row
-    # maximum and everything within 2^-14 of it in)
+    # (2^-4 for values in the normal range, which the gain of 16 keeps the
+    # row maximum and everything within 2^-10 of it in)
     _, lse_sim = oracle.attention_fp8_simulated(q, k, v, signs, 0.125)
     dl = np.abs(lse_p - lse_sim)
     assert 0 < dl.max() <= np.log1p(2.0 ** -4)
@@ -321,6 +323,54 @@ def test_fp8_simulation_quantized_p_keeps_constant_v():
     for causal in (False, True):
         o_p, _ = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, causal=causal, quantize_p=True)
         np.testing.assert_allclose(o_p, v, rtol=1e-13, atol=0)
+
+
+def test_quantized_probabilities_closed_forms():
+    """The rounded weights of the FP8 second product on hand-computed rows.
+    Scores 0 and ln 0.3 (log2: 0 and -1.737): M = 0, P' = E4M3(16) = 16 and
+    E4M3(4.8) = 5 (spacing 0.5 in [4, 8)), so P~ = (1, 5/16).  A V block scale
+    of 0.75 of the largest makes the second gain 12: E4M3(3.6) = 3.5 (spacing
+    0.25 in [2, 4)), P~ = 3.5/12.  A zero scale counts as the largest one."""
+    s = np.array([[0.0, np.log(0.3)]])
+    pq, m = oracle.quantized_probabilities(s, np.array([2.0, 2.0]))
+    assert m[0] == 0.0
+    np.testing.assert_array_equal(pq, [[1.0, 5 / 16]])
+    pq, _ = oracle.quantized_probabilities(s, np.array([2.0, 1.5]))
+    np.testing.assert_array_equal(pq, [[1.0, 3.5 / 12]])
+    pq, _ = oracle.quantized_probabilities(s, np.array([2.0, 0.0]))
+    np.testing.assert_array_equal(pq, [[1.0, 5 / 16]])
+    pq, _ = oracle.quantized_probabilities(s, np.array([0.0, 0.0]))
+    np.testing.assert_array_equal(pq, [[1.0, 5 / 16]])
+    # the reference is the row maximum rounded UP to a power of two: scores
+    # log2 0.7 and -inf (masked) give M = 0, P' = E4M3(11.2) = 11 (spacing 1
+    # in [8, 16)); the masked key weighs exactly 0
+    pq, m = oracle.quantized_probabilities(np.array([[np.log(0.7), -np.inf]]), np.array([1.0, 1.0]))
+    assert m[0] == 0.0
+    np.testing.assert_array_equal(pq, [[11 / 16, 0.0]])
+    # weights far below the row maximum fall into E4M3's subnormals (spacing
+    # 2^-9 of the gained value): 2^-12 * 16 = 2^-8 is the subnormal 2 * 2^-9
+    pq, _ = oracle.quantized_probabilities(np.array([[0.0, -12 * np.log(2.0)]]), np.array([1.0, 1.0]))
+    np.testing.assert_array_equal(pq, [[1.0, 2.0 ** -12]])
+    pq, _ = oracle.quantized_probabilities(np.array([[0.0, -13.5 * np.log(2.0)]]), np.array([1.0, 1.0]))
+    assert pq[0, 1] == 2.0 ** -13        # 2^-13.5 * 16 = 0.707 * 2^-9 rounds up to one subnormal step
+    pq, _ = oracle.quantized_probabilities(np.array([[0.0, -14.5 * np.log(2.0)]]), np.array([1.0, 1.0]))
+    assert pq[0, 1] == 0.0               # 0.354 * 2^-9 rounds to zero
+
+
+def test_quantized_probabilities_power_of_two_shift():
+    """Shifting a row's scores by k ln 2 (k an integer) moves M by k and
+    leaves the rounded weights unchanged: the grid is tied to powers of two,
+    not to the exact maximum.  A non-integer shift changes them."""
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((5, 300)) * 3
+    w = rng.uniform(0.2, 1.0, 300)
+    pq, m = oracle.quantized_probabilities(s, w)
+    for kk in (-3, 1, 7):
+        pk, mk = oracle.quantized_probabilities(s + kk * np.log(2.0), w)
+        np.testing.assert_array_equal(mk, m + kk)
+        np.testing.assert_allclose(pk, pq, rtol=1e-12, atol=0)
+    p_half, _ = oracle.quantized_probabilities(s + 0.5 * np.log(2.0), w)
+    assert np.abs(p_half / np.exp(0.5 * np.log(2.0)) - pq).max() > 1e-3
 
 
 def test_rel_rms():
