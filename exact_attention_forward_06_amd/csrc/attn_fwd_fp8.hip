@@ -13,13 +13,24 @@
 //  * S: one 32x32x64 MFMA per 64 of d.  128-row workgroups and 64-key tiles
 //    never straddle a 128-row scale block, so sQ * sK * softmax_scale *
 //    log2(e) is ONE scalar per tile.
-//  * Lazy rescale with threshold 2^4: P = exp2(s c - m_run) <= 16.
-//  * P V: P is rounded to E4M3 after multiplication by 16 * sV_j / sVmax
-//    (sV_j the tile's V block scale, sVmax the largest V block scale of the
-//    head); the factor enters the exp2 argument as a per-row bias, keeps
-//    P' <= 256 < 448 (no saturation) and keeps values down to 2^-10 of the
-//    row maximum out of the E4M3 subnormals.  At the end
-//    O = acc * sVmax / 16 / l.
+//  * Lazy rescale of O with threshold 2^4: the running max m_run that O and
+//    l are kept relative to is a whole number (log2 units, rounded up when
+//    it moves), so the rescale factors are exact powers of two.
+//  * P V: P is rounded to E4M3 against its own reference m_ref, the running
+//    row maximum after the tile, rounded up to a whole number -- the m of
+//    the tiled online softmax of the "FlashAttention-2/3" page ("技术原理"),
+//    so the rounding does not depend on the lazy threshold -- after
+//    multiplication by the gain 256 sV_j / sVmax (sV_j the tile's V block
+//    scale, sVmax the largest V block scale of the head; an all-zero V block,
+//    scale 0, takes the gain of sVmax, and its codes contribute nothing).
+//    The gain enters the exp2 argument as a per-row bias and keeps
+//    P' <= 256 < 448 (no saturation).  The difference between the two
+//    references, 2^(m_ref - m_run) with 0 <= m_ref - m_run <= 4, is applied
+//    exactly by the MFMA's per-lane E8M0 scale of the P'^T operand (lane n
+//    and n + 32 hold query n).  At the end O = acc * sVmax / 256 / l.
+//  * Q and K block scales of 0 (all-zero blocks, all codes 0) are used as 1:
+//    the scores are 0 either way, and a zero factor would turn the -inf of
+//    masked scores into NaN.
 //  * Row sums l add up the E4M3-rounded P' (over the tile's gain), so O is
 //    normalised by exactly the weights its second product used (rows of the
 //    effective P sum to 1) and the LSE is the log of that normaliser.  The
@@ -46,7 +57,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 constexpr float kTau8 = 4.f;         // lazy-rescale threshold (log2 units)
-constexpr float kPGain = 16.f;       // P' = P * kPGain * sV_j / sVmax <= 2^kTau8 * 16 = 256
+constexpr float kPGain = 256.f;      // P' = P * kPGain * sV_j / sVmax <= 256, P relative to m_ref
 
 struct F8Params {
   const uint8_t* q8;
@@ -72,6 +83,18 @@ __device__ __forceinline__ int key_of_row8(int r) { return (((r >> 2) & 1) << 4)
 template <int FA, int FB>
 __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+}
+
+// The same with a per-lane E8M0 scale of the B operand (127 = 1.0): lane
+// (n, g) scales the 32 K-values of column n it holds by 2^(sb - 127).
+template <int FA, int FB>
+__device__ __forceinline__ f32x16_t mfma_fp8_sb(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, sb);
+}
+
+// E8M0 byte of 2^(m_ref - m_run) (both whole numbers, m_ref >= m_run).
+__device__ __forceinline__ int ref_scale(float m_ref, float m_run) {
+  return m_ref == -INFINITY ? 127 : 127 + (int)(m_ref - m_run);
 }
 
 __device__ __forceinline__ i32x8_t cat(u32x4_t lo, u32x4_t hi) {
@@ -148,10 +171,12 @@ void attn_fwd_fp8_kernel(F8Params p) {
   const int64_t head = (int64_t)bh * N * D;
   const float* ksc = p.ks + (int64_t)bh * p.nblk;
   const float* vsc = p.vs + (int64_t)bh * p.nblk;
-  const float sq = p.qs[(int64_t)bh * p.nblk + mb];
+  const float sq_raw = p.qs[(int64_t)bh * p.nblk + mb];
+  const float sq = sq_raw > 0.f ? sq_raw : 1.f;
 
   float svmax = 0.f;
   for (int i = 0; i < p.nblk; ++i) svmax = fmaxf(svmax, vsc[i]);
+  if (!(svmax > 0.f)) svmax = 1.f;     // every V block is zero: O = 0
   const float inv_svmax = 1.f / svmax;
 
   // Q8^T fragments: lane (n, g) holds Q8[q][64 ks + 32 g .. +32]
@@ -206,7 +231,8 @@ void attn_fwd_fp8_kernel(F8Params p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;   // reference of O and l
+  float m_ref = -INFINITY;   // reference of P': ceil of the running row max
   float l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
@@ -214,8 +240,10 @@ void attn_fwd_fp8_kernel(F8Params p) {
   const float c0 = sq * p.scale_log2;
 
   auto compute_tile = [&](int kt0, const char* sb) __attribute__((always_inline)) {
-    const float c = c0 * ksc[kt0 >> 7];
-    const float fv = vsc[kt0 >> 7] * inv_svmax;     // in (0, 1]
+    const float ks_raw = ksc[kt0 >> 7];
+    const float c = c0 * (ks_raw > 0.f ? ks_raw : 1.f);
+    const float sv = vsc[kt0 >> 7];
+    const float fv = sv > 0.f ? sv * inv_svmax : 1.f;     // in (0, 1]
 
     f32x16_t sacc[NKB];
 #pragma unroll
@@ -247,8 +275,8 @@ void attn_fwd_fp8_kernel(F8Params p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     const float m_tile = pair_max(mx) * c;
     if (__any(m_tile > m_run + kTau8)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      const float m_new = ceilf(fmaxf(m_run, m_tile));   // whole number (or -inf)
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - m_new));
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -256,8 +284,10 @@ void attn_fwd_fp8_kernel(F8Params p) {
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    // e = P * kPGain * fv  with P = exp2(s c - m_use)
+    m_ref = fmaxf(m_ref, ceilf(m_tile));
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    const int psc = ref_scale(m_ref, m_run);
+    // e = P * kPGain * fv  with P = exp2(s c - m_ref)
     const float lg = __builtin_amdgcn_logf(kPGain * fv);   // v_log_f32 is log2
     const float bias = lg - m_use;
 #pragma unroll
@@ -282,7 +312,7 @@ void attn_fwd_fp8_kernel(F8Params p) {
         rs0 += r01[0] + r23[0];
         rs1 += r01[1] + r23[1];
       }
-    l_run += (rs0 + rs1) * (1.f / (kPGain * fv));
+    l_run += __builtin_amdgcn_ldexpf((rs0 + rs1) * (1.f / (kPGain * fv)), psc - 127);
 
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -290,7 +320,7 @@ void attn_fwd_fp8_kernel(F8Params p) {
       for (int t = 0; t < NPV; ++t) {
         const i32x8_t a = cat(*(const lds_u32x4_t*)(sb + db * 32 * VRB + vaddr[t][0]),
                               *(const lds_u32x4_t*)(sb + db * 32 * VRB + vaddr[t][1]));
-        oacc[db] = mfma_fp8<FMT, 0>(a, pf[t], oacc[db]);
+        oacc[db] = mfma_fp8_sb<FMT, 0>(a, pf[t], oacc[db], psc);
       }
   };
 
@@ -336,7 +366,7 @@ void attn_fwd_fp8_kernel(F8Params p) {
 // SIMD; waves 0-3 and 4-7 alternate, one phase apart, between an MFMA phase
 // (S_j^T = K8_j Q8^T and O^T += V8_{j-1}^T P8_{j-1}^T) and a softmax phase
 // (mask, scale, row max, lazy rescale, P' = exp2(s c + bias) rounded to
-// E4M3), with a workgroup barrier between phases.  The MFMA phase also forms
+// E4M3 against m_ref), with a workgroup barrier between phases.  The MFMA phase also forms
 // the row sums of the previous tile's rounded P' (ones x P'^T); the next
 // softmax phase adds them, divided by that tile's gain, to l before its own
 // rescale, as they are relative to the same running max.  Every wave's 32
@@ -403,10 +433,12 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   typedef __attribute__((address_space(4))) const float cfloat_t;
   cfloat_t* ksc = (cfloat_t*)(p.ks + (int64_t)bh * p.nblk);
   cfloat_t* vsc = (cfloat_t*)(p.vs + (int64_t)bh * p.nblk);
-  const float sq = (wq0 < N) ? p.qs[(int64_t)bh * p.nblk + (wq0 >> 7)] : 1.f;
+  const float sq_raw = (wq0 < N) ? p.qs[(int64_t)bh * p.nblk + (wq0 >> 7)] : 1.f;
+  const float sq = sq_raw > 0.f ? sq_raw : 1.f;
 
   float svmax = 0.f;
   for (int i = 0; i < p.nblk; ++i) svmax = fmaxf(svmax, vsc[i]);
+  if (!(svmax > 0.f)) svmax = 1.f;     // every V block is zero: O = 0
   const float inv_svmax = 1.f / svmax;
 
   // Q8^T fragments: lane (n, g) holds Q8[q][64 ks + 32 g .. +32]
@@ -461,7 +493,8 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;   // reference of O and l
+  float m_ref = -INFINITY;   // reference of P': ceil of the running row max
   float l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
@@ -485,6 +518,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
   float inv_gain_prev = 0.f;     // 1 / (kPGain * fv) of the tile whose P' is in pf
+  int psc_prev = 127;            // E8M0 scale 2^(m_ref - m_run) of the P' in pf
 
   // MFMA phase: S^T of tile j and O^T += V^T P^T of tile j-1, operands read
   // LA MFMA pairs ahead; pair i = S block i % NKB, K-step i / NKB and O block
@@ -508,16 +542,16 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     for (int i = 0; i < NOPS; ++i) {
       if (i + LA < NOPS) load(i + LA);
       sacc[i % NKB] = mfma_fp8<FMT, FMT>(kf[i], qf[i / NKB], sacc[i % NKB]);
-      oacc[i % NDB] = mfma_fp8<FMT, 0>(vf[i], pf[i / NDB], oacc[i % NDB]);
+      oacc[i % NDB] = mfma_fp8_sb<FMT, 0>(vf[i], pf[i / NDB], oacc[i % NDB], psc_prev);
       __builtin_amdgcn_sched_barrier(0);
     }
     {
       f32x16_t z;
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = 0.f;
-      lacc = mfma_fp8<0, 0>(ones, pf[0], z);
+      lacc = mfma_fp8_sb<0, 0>(ones, pf[0], z, psc_prev);
 #pragma unroll
-      for (int t = 1; t < NPV; ++t) lacc = mfma_fp8<0, 0>(ones, pf[t], lacc);
+      for (int t = 1; t < NPV; ++t) lacc = mfma_fp8_sb<0, 0>(ones, pf[t], lacc, psc_prev);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -530,8 +564,8 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   // softmax phase of tile j (this wave needs it)
   auto phase_softmax = [&](int j) __attribute__((always_inline)) {
     const int kt0 = j * BN;
-    const float c = c0 * ks_next;
-    const float fv = vs_next * inv_svmax;     // in (0, 1]
+    const float c = c0 * (ks_next > 0.f ? ks_next : 1.f);
+    const float fv = vs_next > 0.f ? vs_next * inv_svmax : 1.f;     // in (0, 1]
     {
       const int jn = j + 1 < w_tiles ? j + 1 : j;
       ks_next = ksc[jn];
@@ -554,8 +588,8 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
     const float m_tile = pair_max(mx) * c;
     l_run = fmaf(lacc[0], inv_gain_prev, l_run);   // previous tile, same m_run as its P'
     if (__any(m_tile > m_run + kTau8)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      const float m_new = ceilf(fmaxf(m_run, m_tile));   // whole number (or -inf)
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - m_new));
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -563,9 +597,11 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    m_ref = fmaxf(m_ref, ceilf(m_tile));
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     const float bias = __builtin_amdgcn_logf(kPGain * fv) - m_use;   // v_log_f32 is log2
     inv_gain_prev = __builtin_amdgcn_rcpf(kPGain * fv);
+    psc_prev = ref_scale(m_ref, m_run);
 #pragma unroll
     for (int t = 0; t < NPV; ++t)
 #pragma unroll

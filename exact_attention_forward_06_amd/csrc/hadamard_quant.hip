@@ -248,7 +248,7 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p, typename 
   // so a quotient that is representable (e.g. an exact E4M3 rounding tie,
   // frequent for 16-bit inputs whose x * 448 is exact) comes out exactly.
   const float ramax = amax > 0.f ? 1.f / amax : 0.f;
-  if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax > 0.f ? amax * p.scale_norm / QMAX : 1.f;
+  if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax * p.scale_norm / QMAX;   // 0 for a zero block
 
   // codes
   uint8_t* out = p.x8 + (int64_t)bh * p.N * D;

@@ -180,7 +180,7 @@ int attn_merge(int out_dtype, int S, int B, int H, int N, int d,
  * with D = diag(signs) and H the Sylvester-order Hadamard matrix
  * (H[i][j] = (-1)^popcount(i & j)); otherwise x~ = x.  Then, per
  * (b, h, block of block_rows consecutive rows) over all d columns:
- * amax = max |x~|, scale = amax / Q (1 if amax = 0), and
+ * amax = max |x~|, scale = amax / Q (0 for an all-zero block), and
  * code = round-to-nearest-even of x~ * Q / amax in the chosen format, with
  * Q = 448 for OCP E4M3 (bias 7) and Q = 57344 for OCP E5M2 (bias 15).
  * Dequantisation is x~ = decode(code) * scale.
@@ -222,11 +222,14 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  * Both products run on FP8 MFMA with fp32 accumulation: S = Q8 K8^T with
  * the two block scales and softmax_scale folded into one factor per tile,
  * and O += P V where P is rounded to E4M3 (whatever fp8_format is) after
- * multiplication by a gain
- * of 16 * sV_j / max_j sV_j (sV_j the scale of V's key block j), so that
- * the V block scales fold into P and the lazy rescale threshold of 2^4
- * keeps the scaled P at most 256.  The row sums l are those of the rounded
- * P (each tile's sum divided by its gain), so O is normalised by exactly the
+ * multiplication by a gain of 256 * w_j / max_j sV_j (w_j = sV_j, the scale
+ * of V's key block j, or max_j sV_j for an all-zero block), so that the V
+ * block scales fold into P.  P is taken relative to the running row maximum
+ * of the online pass after each block of B_c keys (B_c = 128 for d <= 128,
+ * 64 for d = 256), rounded up to a whole number in log2 units, so the
+ * rounding grid is that of 2^(s log2 e) times a power of two and the scaled
+ * P is at most 256.  The row sums l are those of the rounded P (each
+ * block's sum divided by its gain), so O is normalised by exactly the
  * weights its second product used, and lse is m + log(l) of that
  * normaliser: it lies within log(1 + 2^-4) of the logsumexp of the
  * dequantised scores (E4M3 keeps 3 mantissa bits) for rows whose scaled P

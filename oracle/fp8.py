@@ -199,7 +199,7 @@ def dequantize(codes, scales, block_rows=128, transposed=False, fmt="e4m3"):
 
 
 def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
-                            quantize_p=False, fmt="e4m3"):
+                            quantize_p=False, fmt="e4m3", p_block=128):
     """Step-by-step simulation of FP8 attention.
 
     1. Rotate Q and K with the shared signs (skipped if signs is None).
@@ -208,21 +208,15 @@ def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
 
     With quantize_p the probabilities of the second product are rounded to
     E4M3 as well (the pages put both products on the FP8 path but leave the
-    rounding of P open).  Reading, per head and query row i:
-      * t_ij = s_ij log2(e) (scores in log2 units, masked ones -inf) and
-        M_i = ceil(max_j t_ij): the row's reference is a power of two, so the
-        rounding grid of the weights does not depend on where exactly the
-        maximum lies;
-      * V's block scale is folded into the weight before rounding: with
-        w_j the scale of key j's V block (the largest V block scale of the
-        head, svmax, for an all-zero block, whose codes contribute nothing)
-        and gain g_j = 16 w_j / svmax,
-            P'_ij = E4M3(2^(t_ij - M_i) g_j),   P~_ij = P'_ij / g_j;
-      * the rounded weights serve both the product with V and the row sums:
-            l_i = sum_j P~_ij,  O_i = sum_j P~_ij V^_j / l_i,
-            LSE_i = M_i ln 2 + ln l_i,
-        so O is normalised by exactly the weights it used (a constant V comes
-        out unchanged).
+    rounding of P open).  Reading: the weights are rounded as the tiled
+    online softmax of the "FlashAttention-2/3" page (section "技术原理")
+    produces them, block by block of p_block keys, against the running row
+    maximum after that block, rounded up to a power of two; each V block's
+    dequantisation scale is folded into the weight before rounding
+    (quantized_probabilities states the rounding); the rounded weights serve
+    both the product with V and the row sums, so O is normalised by exactly
+    the weights it used (a constant V comes out unchanged) and
+    LSE = M ln 2 + ln l.
     Returns fp64 (O, LSE).
     """
     qc, qs, _ = hadamard_rotate_quant(q, signs, block_rows, fmt=fmt)
@@ -244,28 +238,48 @@ def attention_fp8_simulated(q, k, v, signs, scale, causal=False, block_rows=128,
         if causal:
             s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
         w = np.repeat(vsf[h], block_rows)[:n]
-        pq, m = quantized_probabilities(s, w)
+        pq, m = quantized_probabilities(s, w, p_block)
         l = pq.sum(1)
         o[h] = (pq @ vf[h]) / l[:, None]
         lse[h] = m * np.log(2.0) + np.log(l)
     return o.reshape(*lead, n, -1), lse.reshape(*lead, n)
 
 
-def quantized_probabilities(s, w):
-    """The E4M3-rounded weights of the FP8 second product (the reading stated
-    in attention_fp8_simulated).  s: scores [Nq, Nk] in natural units
-    (masked entries -inf); w: [Nk] the V block scale of each key.  Returns
-    (P~ [Nq, Nk], M [Nq]) with M_i = ceil(max_j s_ij log2 e) and
-    P~_ij = E4M3(2^(s_ij log2 e - M_i) g_j) / g_j, g_j = 16 w_j / svmax
-    (w_j = svmax for a zero scale; svmax = 1 if every scale is zero)."""
+P_GAIN = 256.0   # largest E4M3 weight: 256 <= 448, so nothing saturates
+
+
+def quantized_probabilities(s, w, block=128):
+    """The E4M3-rounded weights of the FP8 second product.
+
+    s: scores [Nq, Nk] in natural units (masked entries -inf); w: [Nk] the
+    dequantisation scale of each key's V block; block: keys per block of the
+    online pass.  With t = s log2(e) and b(j) the block of key j:
+      * M_i^b = ceil(max of t_ik over the keys k of blocks 0..b): the running
+        row maximum after block b (the online softmax's m), rounded up to a
+        whole power of two;
+      * gain g_j = 256 w_j / svmax (svmax the largest V block scale; a zero
+        scale, an all-zero block whose values contribute nothing, counts as
+        svmax; svmax = 1 if every scale is zero);
+      * P'_ij = E4M3(2^(t_ij - M_i^b(j)) g_j): at most 256, no saturation;
+        weights far below the running maximum fall into E4M3's subnormals;
+      * weight_ij = P'_ij / g_j * 2^(M_i^b(j) - M_i), M_i = M_i^last.
+    Returns (weights [Nq, Nk], M [Nq]): the weights relative to 2^M_i."""
     s = np.asarray(s, np.float64)
     w = np.asarray(w, np.float64)
+    nq, nk = s.shape
     t = s * np.log2(np.e)
-    m = np.ceil(np.max(t, axis=1))
+    nb = -(-nk // block)
+    bmax = np.stack([np.max(t[:, b * block:(b + 1) * block], axis=1) for b in range(nb)], axis=1)
+    ref_blk = np.ceil(np.maximum.accumulate(bmax, axis=1))          # [Nq, nb], -inf while all masked
+    ref = np.repeat(ref_blk, block, axis=1)[:, :nk]
+    m = ref_blk[:, -1]
     svmax = float(np.max(w)) if np.max(w) > 0 else 1.0
     w = np.where(w > 0, w, svmax)
-    gain = 16.0 * w / svmax
-    pq = e4m3_decode(e4m3_encode(np.exp2(t - m[:, None]) * gain[None, :])) / gain[None, :]
+    gain = P_GAIN * w / svmax
+    seen = np.isfinite(t)
+    arg = np.where(seen, t - np.where(seen, ref, 0.0), -np.inf)
+    pq = e4m3_decode(e4m3_encode(np.exp2(arg) * gain[None, :])) / gain[None, :]
+    pq = pq * np.exp2(np.where(seen, ref - m[:, None], 0.0))
     return pq, m
 
 

@@ -1,18 +1,33 @@
 """GPU parity of the FP8 path: hadamard_rotate_quant codes/scales against the
 oracle codec, and attn_fwd_fp8 against the oracle's step-by-step FP8
-simulation (rotate -> per-block E4M3 -> exact softmax on the dequantised
-values).
+simulation (rotate -> per-block E4M3 -> softmax on the dequantised values,
+with the probabilities of the second product rounded to E4M3 as
+oracle.quantized_probabilities states: the kernel's reading).
 
 Code parity: a code must equal the oracle's, except where the exact value
 x~ * 448 / amax lies within fp32 rounding of a rounding midpoint; there the
 adjacent code is also accepted (the kernel forms x~ in fp32, the oracle in
 fp64).  Scales: relative 2e-6.
-Attention parity: relative RMS (||O_gpu - O_sim|| / ||O_sim||) <= 3e-2.  The
-kernel also rounds P to E4M3 (a kernel-internal step the pages leave open),
-which the simulation does not; its effect is part of that tolerance.  The row
-sums add up the rounded P, so the LSE may differ from the simulation's by at
-most log(1 + 2^-4), the E4M3 relative rounding bound, and a constant V comes
-out unchanged.
+
+Attention parity against that simulation (the rotated path and every
+input without outlier channels): relative RMS of O <= 3e-3; LSE mean
+|err| <= 3e-4 and 99th percentile <= 1e-2.  What separates the two is the
+bf16 rounding of O (1.66e-3 relative RMS on Gaussian values by itself),
+fp32 accumulation, and weights whose exponent lies within the arithmetic's
+error of an E4M3 rounding midpoint: rare, but when it is a row's dominant
+weight it moves that row's sum by up to an E4M3 step, hence a percentile
+rather than a max for the LSE.  Rows with outlier-sized scores (|s log2 e|
+in the hundreds) widen that error: the FP8 MFMA adds its 64 products with
+less precision than fp32 when one product dominates (measured on gfx950: up
+to ~1 code unit on sums of ~5e3, where an fp32 sum is within 1e-2), so the
+exponents of such rows carry errors of ~1e-3..1e-2.  The unrotated codes of
+the outlier workload, where every score is dominated by the outlier
+channel's product, are checked at relative RMS <= 1e-2 and LSE mean
+<= 1e-2 for that reason.
+
+The error against EXACT attention is a property of the format, measured and
+reported beside the gate the method was set (relative RMS <= 3e-2): on the
+FP8 workload the quantisation alone puts the result well above it.
 """
 import math
 
@@ -23,6 +38,13 @@ import torch
 import oracle
 from exact_attention_forward_06_amd import attn_fwd_fp8, attn_fwd_fp8_e2e, hadamard_rotate_quant
 from exact_attention_forward_06_amd.inputs import WORKLOADS, make_inputs, random_signs, to_f64, workload_inputs
+
+from oracle_pool import fp8_head_errors, map_heads, reduce_fp8
+
+O_TOL = 3e-3          # relative RMS of O against the simulation with rounded P
+LSE_TOL = 1e-2        # 99th percentile of |LSE err| against the same
+LSE_MEAN_TOL = 3e-4   # mean |LSE err| against the same
+UNROT_TOL = 1e-2      # O relative RMS and LSE mean, unrotated codes of outlier inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -93,13 +115,13 @@ def test_hadamard_block_max_encodes_to_448():
     assert np.all(np.max(c & 0x7F, axis=-1) == 0x7E)
 
 
-def test_hadamard_zero_block_unit_scale():
+def test_hadamard_zero_block_zero_scale():
     x = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16)
     x[0, 0, 200, 5] = -3.0
     codes, scales = hadamard_rotate_quant(x.cuda(), None)
     torch.cuda.synchronize()
     s = scales.cpu().numpy()[0, 0]
-    assert s[0] == 1.0 and s[1] == np.float32(3.0 / 448)
+    assert s[0] == 0.0 and s[1] == np.float32(3.0 / 448)
     assert np.all(codes.cpu().numpy()[0, 0, :128] & 0x7F == 0)
     assert codes.cpu().numpy()[0, 0, 200, 5] == 0xFE
 
@@ -111,20 +133,33 @@ def _fp8_inputs(B, H, N, d, seed, outliers=True):
     return inp
 
 
-def _sim_rows(inp, heads, rows_per_head, causal, rotate=True, fmt="e4m3"):
-    """Oracle FP8 simulation and exact attention on sampled rows of the given heads."""
-    q, k, v = inp["q"], inp["k"], inp["v"]
-    d = q.shape[-1]
-    s = 1 / math.sqrt(d)
-    signs = inp["signs"].numpy() if rotate else None
-    sims, exact = [], []
-    for (b, h), rows in zip(heads, rows_per_head):
-        qh = oracle.dequantize(*oracle.hadamard_rotate_quant(to_f64(q[b, h]), signs, 128, fmt=fmt)[:2], 128, fmt=fmt)
-        kh = oracle.dequantize(*oracle.hadamard_rotate_quant(to_f64(k[b, h]), signs, 128, fmt=fmt)[:2], 128, fmt=fmt)
-        vh = oracle.dequantize(*oracle.hadamard_rotate_quant(to_f64(v[b, h]), None, 128, fmt=fmt)[:2], 128, fmt=fmt)
-        sims.append(oracle.attention_rows(qh, kh, vh, rows, s, causal)[0])
-        exact.append(oracle.attention_rows(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), rows, s, causal)[0])
-    return np.concatenate(sims), np.concatenate(exact)
+def p_block(d):
+    """Keys per block of the kernels' online pass (the reference P is
+    rounded against moves once per block): 128 for d <= 128, 64 for d = 256."""
+    return 128 if d <= 128 else 64
+
+
+def _sim_p(inp, causal, rotate=True, fmt="e4m3", v=None):
+    """The oracle's FP8 simulation with rounded P (fp64 O, LSE) for all heads."""
+    d = inp["q"].shape[-1]
+    vv = to_f64(inp["v"] if v is None else v)
+    return oracle.attention_fp8_simulated(to_f64(inp["q"]), to_f64(inp["k"]), vv,
+                                          inp["signs"].numpy() if rotate else None, 1 / math.sqrt(d),
+                                          causal, quantize_p=True, fmt=fmt, p_block=p_block(d))
+
+
+def _check_sim(o, lse, o_ref, lse_ref, what):
+    og = to_f64(o)
+    assert np.all(np.isfinite(og)), what
+    err = oracle.rel_rms(og, o_ref)
+    ld = np.abs(lse.cpu().double().numpy() - lse_ref).ravel()
+    p99 = float(np.quantile(ld, 0.99))
+    print(f"[{what}] vs FP8 simulation: O rel RMS {err:.2e}, LSE mean {ld.mean():.2e} p99 {p99:.2e} "
+          f"max {ld.max():.2e}", flush=True)
+    assert err <= O_TOL, f"{what}: rel RMS vs FP8 simulation {err:.3e} > {O_TOL}"
+    assert ld.mean() <= LSE_MEAN_TOL, f"{what}: mean |LSE err| vs FP8 simulation {ld.mean():.3e}"
+    assert p99 <= LSE_TOL, f"{what}: 99th percentile |LSE err| vs FP8 simulation {p99:.3e} > {LSE_TOL}"
+    return err, ld.max()
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
@@ -137,15 +172,48 @@ def test_fp8_attention_matches_simulation(d, causal, outliers, fmt):
     o, lse = attn_fwd_fp8_e2e(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["signs"].cuda(),
                               causal=causal, fp8_format=fmt)
     torch.cuda.synchronize()
-    rows = np.arange(N)
-    heads = [(0, 0), (0, 1)]
-    sim, exact = _sim_rows(inp, heads, [rows, rows], causal, fmt=fmt)
-    og = np.concatenate([to_f64(o[b, h]) for b, h in heads])
-    err = oracle.rel_rms(og, sim)
-    assert np.all(np.isfinite(og))
-    assert err <= 3e-2, f"rel RMS vs FP8 simulation {err:.4f}"
+    o_ref, lse_ref = _sim_p(inp, causal, fmt=fmt)
+    _check_sim(o, lse, o_ref, lse_ref, f"{fmt} d={d} causal={causal} outliers={outliers}")
     # the quantisation error itself stays in the range E4M3 allows
-    assert oracle.rel_rms(og, exact) < 0.5
+    exact, _ = oracle.attention(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), 1 / math.sqrt(d), causal)
+    assert oracle.rel_rms(to_f64(o), exact) < 0.5
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("case", ["zero_block", "small_v", "zero_block_small_v", "uneven_blocks"])
+def test_fp8_v_block_scales(d, case):
+    """V blocks whose scales differ widely: an all-zero 128-row block (scale
+    0, as padding to a multiple of 128 rows gives), V at 1e-3 of unit scale,
+    both at once, and one block 100x larger than the rest.  The kernel must
+    follow the simulation's reading (zero blocks take the largest scale's
+    gain, the others 16 sV_j / sVmax) to the same tolerance."""
+    B, H, N = 1, 2, 512
+    inp = _fp8_inputs(B, H, N, d, seed=d + 51, outliers=False)
+    v = inp["v"].float()
+    if case in ("small_v", "zero_block_small_v"):
+        v = v * 1e-3
+    if case in ("zero_block", "zero_block_small_v"):
+        v[:, :, 256:384] = 0
+    if case == "uneven_blocks":
+        v[:, :, 128:256] *= 100
+    v = v.to(torch.bfloat16)
+    for causal in (False, True):
+        o, lse = attn_fwd_fp8_e2e(inp["q"].cuda(), inp["k"].cuda(), v.cuda(), inp["signs"].cuda(), causal=causal)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = _sim_p(inp, causal, v=v)
+        _check_sim(o, lse, o_ref, lse_ref, f"{case} d={d} causal={causal}")
+
+
+def test_fp8_all_zero_v():
+    B, H, N, d = 1, 2, 256, 128
+    inp = _fp8_inputs(B, H, N, d, seed=5, outliers=False)
+    v = torch.zeros(B, H, N, d, dtype=torch.bfloat16, device="cuda")
+    for causal in (False, True):
+        o, lse = attn_fwd_fp8_e2e(inp["q"].cuda(), inp["k"].cuda(), v, inp["signs"].cuda(), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o, torch.zeros_like(o))
+        _, lse_ref = _sim_p(inp, causal, v=v.cpu())
+        assert np.abs(lse.cpu().double().numpy() - lse_ref).max() <= 1e-3
 
 
 def test_fp8_lse_close_to_simulated():
@@ -181,34 +249,75 @@ def test_fp8_constant_v_is_returned_exactly(d, causal, fmt):
     assert torch.isfinite(lse).all()
 
 
-def test_fp8_workload_sampled_and_rotation_report(capsys):
-    """The FP8 workload at full size (the bench's launch configuration): parity
-    with the simulation on sampled rows of several heads, and the error
-    against exact attention with and without the Hadamard rotation."""
+def test_fp8_workload_sampled(capsys):
+    """The FP8 workload at full size (the bench's launch configuration) on
+    sampled heads: a fast variant of test_fp8_workload_full."""
     w = WORKLOADS["fp8_hadamard_8k"]
     inp = workload_inputs(w)
     q, k, v, sg = (inp[n].cuda() for n in ("q", "k", "v", "signs"))
-    o_rot, _ = attn_fwd_fp8_e2e(q, k, v, sg)
-    q8, sq = hadamard_rotate_quant(q, None)
-    k8, sk = hadamard_rotate_quant(k, None)
-    v8, sv = hadamard_rotate_quant(v, None, transpose_out=True)
-    o_plain, _ = attn_fwd_fp8(q8, sq, k8, sk, v8, sv)
+    o, lse = attn_fwd_fp8_e2e(q, k, v, sg)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     heads = [(0, 0), (1, 15), (0, 7), (1, 3)]
-    rows = [np.sort(rng.choice(w.N, 96, replace=False)) for _ in heads]
-    sim, exact = _sim_rows(inp, heads, rows, False, rotate=True)
-    sim_plain, _ = _sim_rows(inp, heads, rows, False, rotate=False)
-    og = np.concatenate([to_f64(o_rot[b, h].cpu()[r]) for (b, h), r in zip(heads, rows)])
-    op = np.concatenate([to_f64(o_plain[b, h].cpu()[r]) for (b, h), r in zip(heads, rows)])
-    e_sim = oracle.rel_rms(og, sim)
-    e_sim_plain = oracle.rel_rms(op, sim_plain)
-    assert e_sim <= 3e-2, f"rotated FP8 vs simulation: {e_sim:.4f}"
-    assert e_sim_plain <= 3e-2, f"unrotated FP8 vs simulation: {e_sim_plain:.4f}"
+    tasks = [(inp["q"][b, h].float().numpy(), inp["k"][b, h].float().numpy(), inp["v"][b, h].float().numpy(),
+              inp["signs"].numpy(), o[b, h], lse[b, h], w.scale, False) for b, h in heads]
+    r = reduce_fp8(map_heads(fp8_head_errors, tasks))
     with capsys.disabled():
-        print(f"\n[fp8 workload] rel RMS vs exact: rotated {oracle.rel_rms(og, exact):.4f}, "
-              f"unrotated {oracle.rel_rms(op, exact):.4f}; vs simulation: rotated {e_sim:.4f}, "
-              f"unrotated {e_sim_plain:.4f}", flush=True)
+        print(f"\n[fp8 workload, 4 heads] vs simulation {r['gpu_vs_simp']:.2e}, LSE mean {r['lse_simp_mean']:.2e} "
+              f"p99 {r['lse_simp_p99']:.2e} max {r['lse_simp_max']:.2e}; "
+              f"vs exact {r['gpu_vs_exact']:.4f}", flush=True)
+    assert r["finite"] and r["gpu_vs_simp"] <= O_TOL and r["lse_simp_p99"] <= LSE_TOL, r
+    assert r["lse_simp_mean"] <= LSE_MEAN_TOL, r
+
+
+@pytest.mark.parametrize("rotated", [True, False])
+def test_fp8_workload_full(rotated, capsys):
+    """Every head and row of the FP8 workload (B=2 H=16 N=8192 d=128, one
+    outlier channel x20), rotated (the method) and unrotated (the comparison
+    the pages make):
+      * gate: the GPU against the oracle's simulation with rounded P over all
+        B*H*N*d elements, at O_TOL / LSE_TOL / LSE_MEAN_TOL rotated and at
+        UNROT_TOL unrotated (the FP8 MFMA's coarser sums; module docstring);
+      * reported and checked for consistency: the error against exact
+        attention, which must be the simulation's own error against exact
+        attention (within 5 %): the kernel adds nothing of its own; and the
+        floor of Q, K and V quantisation alone (P exact).
+    The method's gate of relative RMS <= 3e-2 against exact attention is
+    printed as met or NOT MET; on this workload E4M3 puts the result above it
+    ("FlashAttention-3" page, section "FP8 路径与低精度误差", gives the
+    direction of the rotation's effect, not a magnitude)."""
+    w = WORKLOADS["fp8_hadamard_8k"]
+    inp = workload_inputs(w)
+    q, k, v, sg = (inp[n].cuda() for n in ("q", "k", "v", "signs"))
+    if rotated:
+        o, lse = attn_fwd_fp8_e2e(q, k, v, sg)
+    else:
+        q8, sq = hadamard_rotate_quant(q, None)
+        k8, sk = hadamard_rotate_quant(k, None)
+        v8, sv = hadamard_rotate_quant(v, None, transpose_out=True)
+        o, lse = attn_fwd_fp8(q8, sq, k8, sk, v8, sv)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    f32 = {n: inp[n].float().numpy() for n in ("q", "k", "v")}
+    signs = inp["signs"].numpy() if rotated else None
+    tasks = [(f32["q"][b, h], f32["k"][b, h], f32["v"][b, h], signs, o[b, h], lse[b, h], w.scale, False)
+             for b in range(w.B) for h in range(w.H)]
+    r = reduce_fp8(map_heads(fp8_head_errors, tasks))
+    label = "rotated" if rotated else "unrotated"
+    gate = "met" if r["gpu_vs_exact"] <= 3e-2 else "NOT MET"
+    with capsys.disabled():
+        print(f"\n[fp8 workload full, {label}] {r['heads']} heads: GPU vs simulation (rounded P) "
+              f"{r['gpu_vs_simp']:.2e}, |LSE err| mean {r['lse_simp_mean']:.2e} p99 {r['lse_simp_p99']:.2e} "
+              f"max {r['lse_simp_max']:.2e}; rel RMS vs exact: GPU "
+              f"{r['gpu_vs_exact']:.4f}, simulation {r['simp_vs_exact']:.4f}, Q/K/V-only floor "
+              f"{r['floor_vs_exact']:.4f}; gate rel-RMS <= 3e-2 vs exact: {gate}", flush=True)
+    assert r["finite"] and r["heads"] == w.B * w.H
+    if rotated:
+        assert r["gpu_vs_simp"] <= O_TOL and r["lse_simp_p99"] <= LSE_TOL, r
+        assert r["lse_simp_mean"] <= LSE_MEAN_TOL, r
+    else:
+        assert r["gpu_vs_simp"] <= UNROT_TOL and r["lse_simp_mean"] <= UNROT_TOL, r
+    assert abs(r["gpu_vs_exact"] / r["simp_vs_exact"] - 1) <= 0.05, r
 
 
 def test_fp8_outlier_sweep_rotation_on_gpu(capsys):

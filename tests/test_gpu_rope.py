@@ -73,8 +73,8 @@ def test_rope_base_and_e5m2():
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_fp8_attention_with_rope(style, causal):
     """FP8 attention on RoPE'd, rotated, quantised Q and K against the
-    oracle's step-by-step FP8 simulation of the same steps (rel-RMS <= 3e-2,
-    the FP8 parity bar); the error against the exact attention of RoPE(Q),
+    oracle's step-by-step FP8 simulation of the same steps, with rounded P
+    (rel-RMS <= 3e-3, the kernel gate of tests/test_gpu_fp8.py); the error against the exact attention of RoPE(Q),
     RoPE(K) is reported, and must be lower with the rotation than without."""
     B, H, N, d = 1, 2, 1024, 128
     print(f"fp8 attention with rope {style} causal={causal}", flush=True)
@@ -93,5 +93,5 @@ def test_fp8_attention_with_rope(style, causal):
     err, err_nr = oracle.rel_rms(to_f64(o), o_ref), oracle.rel_rms(to_f64(o_nr), o_ref)
     floor = oracle.rel_rms(o_sim, o_ref)
     print(f"vs simulation {err_sim:.4f}; vs exact {err:.4f} (floor {floor:.4f}, unrotated {err_nr:.4f})", flush=True)
-    assert err_sim <= 3e-2
+    assert err_sim <= 3e-3
     assert err < err_nr

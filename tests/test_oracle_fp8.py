@@ -304,8 +304,8 @@ def test_fp8_simulation_error_is_small_but_nonzero():
     o_p, lse_p = oracle.attention_fp8_simulated(q, k, v, signs, 0.125, quantize_p=True)
     assert 0 < oracle.rel_rms(o_p, o_sim) < 0.06
     # rounded P in the row sums: l moves by at most the E4M3 relative rounding
-    # (2^-4 for values in the normal range, which the gain of 16 keeps the
-    # row maximum and everything within 2^-10 of it in)
+    # (2^-4 for values in the normal range, which the gain of 256 keeps the
+    # row maximum and everything within 2^-14 of it in)
     _, lse_sim = oracle.attention_fp8_simulated(q, k, v, signs, 0.125)
     dl = np.abs(lse_p - lse_sim)
     assert 0 < dl.max() <= np.log1p(2.0 ** -4)
@@ -326,35 +326,57 @@ def test_fp8_simulation_quantized_p_keeps_constant_v():
 
 
 def test_quantized_probabilities_closed_forms():
-    """The rounded weights of the FP8 second product on hand-computed rows.
-    Scores 0 and ln 0.3 (log2: 0 and -1.737): M = 0, P' = E4M3(16) = 16 and
-    E4M3(4.8) = 5 (spacing 0.5 in [4, 8)), so P~ = (1, 5/16).  A V block scale
-    of 0.75 of the largest makes the second gain 12: E4M3(3.6) = 3.5 (spacing
-    0.25 in [2, 4)), P~ = 3.5/12.  A zero scale counts as the largest one."""
+    """The rounded weights of the FP8 second product on hand-computed rows
+    (one block).  Scores 0 and ln 0.3 (log2: 0 and -1.737): M = 0,
+    P' = E4M3(256) = 256 and E4M3(76.8) = 80 (spacing 8 in [64, 128)), so
+    P~ = (1, 80/256).  A V block scale of 0.75 of the largest makes the
+    second gain 192: E4M3(57.6) = 56 (spacing 4 in [32, 64)), P~ = 56/192.
+    A zero scale counts as the largest one."""
     s = np.array([[0.0, np.log(0.3)]])
     pq, m = oracle.quantized_probabilities(s, np.array([2.0, 2.0]))
     assert m[0] == 0.0
-    np.testing.assert_array_equal(pq, [[1.0, 5 / 16]])
+    np.testing.assert_array_equal(pq, [[1.0, 80 / 256]])
     pq, _ = oracle.quantized_probabilities(s, np.array([2.0, 1.5]))
-    np.testing.assert_array_equal(pq, [[1.0, 3.5 / 12]])
+    np.testing.assert_array_equal(pq, [[1.0, 56 / 192]])
     pq, _ = oracle.quantized_probabilities(s, np.array([2.0, 0.0]))
-    np.testing.assert_array_equal(pq, [[1.0, 5 / 16]])
+    np.testing.assert_array_equal(pq, [[1.0, 80 / 256]])
     pq, _ = oracle.quantized_probabilities(s, np.array([0.0, 0.0]))
-    np.testing.assert_array_equal(pq, [[1.0, 5 / 16]])
+    np.testing.assert_array_equal(pq, [[1.0, 80 / 256]])
     # the reference is the row maximum rounded UP to a power of two: scores
-    # log2 0.7 and -inf (masked) give M = 0, P' = E4M3(11.2) = 11 (spacing 1
-    # in [8, 16)); the masked key weighs exactly 0
+    # log2 0.7 and -inf (masked) give M = 0, P' = E4M3(179.2) = 176 (spacing
+    # 16 in [128, 256)); the masked key weighs exactly 0
     pq, m = oracle.quantized_probabilities(np.array([[np.log(0.7), -np.inf]]), np.array([1.0, 1.0]))
     assert m[0] == 0.0
-    np.testing.assert_array_equal(pq, [[11 / 16, 0.0]])
+    np.testing.assert_array_equal(pq, [[176 / 256, 0.0]])
     # weights far below the row maximum fall into E4M3's subnormals (spacing
-    # 2^-9 of the gained value): 2^-12 * 16 = 2^-8 is the subnormal 2 * 2^-9
-    pq, _ = oracle.quantized_probabilities(np.array([[0.0, -12 * np.log(2.0)]]), np.array([1.0, 1.0]))
-    np.testing.assert_array_equal(pq, [[1.0, 2.0 ** -12]])
-    pq, _ = oracle.quantized_probabilities(np.array([[0.0, -13.5 * np.log(2.0)]]), np.array([1.0, 1.0]))
-    assert pq[0, 1] == 2.0 ** -13        # 2^-13.5 * 16 = 0.707 * 2^-9 rounds up to one subnormal step
-    pq, _ = oracle.quantized_probabilities(np.array([[0.0, -14.5 * np.log(2.0)]]), np.array([1.0, 1.0]))
-    assert pq[0, 1] == 0.0               # 0.354 * 2^-9 rounds to zero
+    # 2^-9 of the gained value): 2^-12 * 256 = 2^-4 is still normal,
+    # 2^-17.5 * 256 = 0.707 * 2^-9 rounds up to one subnormal step and
+    # 2^-18.5 * 256 = 0.354 * 2^-9 to zero
+    def w2(t2):
+        return oracle.quantized_probabilities(np.array([[0.0, t2 * np.log(2.0)]]), np.array([1.0, 1.0]))[0][0, 1]
+    assert w2(-12.0) == 2.0 ** -12
+    assert w2(-17.5) == 2.0 ** -17
+    assert w2(-18.5) == 0.0
+
+
+def test_quantized_probabilities_running_reference():
+    """Blocks of 2 keys: the weights of block 0 are rounded against the
+    running maximum after block 0, not the row's final maximum.  Block 0
+    holds t = -16.3 and -16 (log2), block 1 holds 0 and -inf.  M^0 = -16:
+    2^-0.3 * 256 = 207.9 rounds to 208, weight 208/256 * 2^-16.  Against the
+    final reference M = 0 it would be the subnormal 2^-16.3 * 256 = 0.0032,
+    rounded to 2 * 2^-9, weight 2^-16.  In the normal range the two agree
+    (the grid is the same up to a power of two)."""
+    t = np.array([[-16.3, -16.0, 0.0, -np.inf]])
+    pq, m = oracle.quantized_probabilities(t * np.log(2.0), np.ones(4), block=2)
+    assert m[0] == 0.0
+    np.testing.assert_array_equal(pq, [[208 / 256 * 2.0 ** -16, 2.0 ** -16, 1.0, 0.0]])
+    pq1, _ = oracle.quantized_probabilities(t * np.log(2.0), np.ones(4), block=4)
+    assert pq1[0, 0] == 2.0 ** -16
+    t = np.array([[-2.5, -2.0, 0.0, -1.0]])
+    pa, _ = oracle.quantized_probabilities(t * np.log(2.0), np.ones(4), block=2)
+    pb, _ = oracle.quantized_probabilities(t * np.log(2.0), np.ones(4), block=4)
+    np.testing.assert_array_equal(pa, pb)
 
 
 def test_quantized_probabilities_power_of_two_shift():
@@ -364,13 +386,14 @@ def test_quantized_probabilities_power_of_two_shift():
     rng = np.random.default_rng(3)
     s = rng.standard_normal((5, 300)) * 3
     w = rng.uniform(0.2, 1.0, 300)
-    pq, m = oracle.quantized_probabilities(s, w)
-    for kk in (-3, 1, 7):
-        pk, mk = oracle.quantized_probabilities(s + kk * np.log(2.0), w)
-        np.testing.assert_array_equal(mk, m + kk)
-        np.testing.assert_allclose(pk, pq, rtol=1e-12, atol=0)
-    p_half, _ = oracle.quantized_probabilities(s + 0.5 * np.log(2.0), w)
-    assert np.abs(p_half / np.exp(0.5 * np.log(2.0)) - pq).max() > 1e-3
+    for block in (7, 128, 300):
+        pq, m = oracle.quantized_probabilities(s, w, block)
+        for kk in (-3, 1, 7):
+            pk, mk = oracle.quantized_probabilities(s + kk * np.log(2.0), w, block)
+            np.testing.assert_array_equal(mk, m + kk)
+            np.testing.assert_allclose(pk, pq, rtol=1e-12, atol=0)
+        p_half, _ = oracle.quantized_probabilities(s + 0.5 * np.log(2.0), w, block)
+        assert np.abs(p_half / np.exp(0.5 * np.log(2.0)) - pq).max() > 1e-3
 
 
 def test_rel_rms():
