@@ -66,6 +66,9 @@ WORKLOADS = {
         Workload("bf16_d64", "bf16", 8, 16, 4096, 64, False, 4),
         Workload("bf16_d256", "bf16", 4, 8, 4096, 256, False, 4),
         Workload("fp8_hadamard_8k", "fp8", 2, 16, 8192, 128, False, 5, outlier_frac=0.005),
+        # non-causal bf16 at the FP8 workload's shape and seed (its Q, K, V
+        # before the outlier channels are scaled): the 16-bit context line
+        Workload("bf16_8k", "bf16", 2, 16, 8192, 128, False, 5),
         Workload("bf16_few_heads_8k", "bf16", 1, 2, 8192, 128, False, 9),
     ]
 }
