@@ -1,7 +1,8 @@
-// Pieces shared by the two 16-bit attention kernels (attn_fwd.hip and
-// attn_fwd_pp.hip): kernel parameters, the MFMA / rounding wrappers, the
-// key permutation of the S^T accumulator, the LDS swizzle and the
-// global -> LDS tile copy.  Private to those translation units.
+// Pieces shared by the attention forward kernels (the 16-bit attn_fwd.hip
+// and attn_fwd_pp.hip, and the fp32 attn_fwd_f32.hip): kernel parameters,
+// the MFMA / rounding wrappers, the key permutation of the S^T accumulator,
+// the LDS swizzle and the global -> LDS tile copy.  Private to those
+// translation units.
 #pragma once
 
 #include "device_common.h"
