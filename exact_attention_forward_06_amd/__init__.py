@@ -16,7 +16,7 @@ Public API (thin wrappers over the C ABI of libattn.so, include/attn.h):
     attn_bwd(q, k, v, o, lse, dout, causal=False) -> (dq, dk, dv, delta)
 """
 from ._lib import (AttnError, attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_merge, hadamard_rotate_quant,
-                   load, rope_hadamard_rotate_quant, splitkv_chunk)
+                   clock_probe, load, rope_hadamard_rotate_quant, splitkv_chunk)
 
 
 def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=None, fp8_format="e4m3",
@@ -37,5 +37,5 @@ def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=No
                         stream=stream, fp8_format=fp8_format)
 
 
-__all__ = ["AttnError", "attn_bwd", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
+__all__ = ["AttnError", "attn_bwd", "clock_probe", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
            "hadamard_rotate_quant", "load", "rope_hadamard_rotate_quant", "splitkv_chunk"]

@@ -11,7 +11,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_LIBRARY names another build of the same library (the host-sanitised
+# build that the ABI tests run under); unset, the in-tree libattn.so.
+LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "include", "attn.h")
 
@@ -39,6 +41,7 @@ _SIGNATURES = {
                                     _vp, _vp], _i),
     "attn_bwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                   ctypes.c_float, _i, _vp], _i),
+    "attn_clock_probe": ([_i, _vp, _vp], _i),
 }
 
 _lib = None
@@ -285,6 +288,17 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, dq=None, d
                         _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)),
                         _stream(stream)))
     return dq, dk, dv, delta
+
+
+def clock_probe(spin_us=300, out=None, stream=None):
+    """Launch the shader-clock probe (a measurement aid): out (device int64
+    [2], allocated if None) receives shader cycles and 100 MHz ticks over
+    spin_us microseconds; MHz = out[0] / out[1] * 100 once the stream has
+    run it."""
+    dev = out.device if out is not None else torch.device("cuda", torch.cuda.current_device())
+    out = _buf(out, (2,), torch.int64, dev, "out")
+    _check(load().attn_clock_probe(int(spin_us), _ptr(out), _stream(stream)))
+    return out
 
 
 def declared_symbols(header: str = HEADER_PATH):

@@ -518,3 +518,14 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
   if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_bwd kernel for dtype %d d=%d", dtype, d);
   return hip_status(e, "attn_bwd launch");
 }
+
+extern "C" int attn_clock_probe(int spin_us, uint64_t* out, void* stream) {
+  if (spin_us < 1 || spin_us > 100000)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "spin_us=%d is not in 1 .. 100000", spin_us);
+  if (out == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "out is NULL");
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "out is not 8-byte aligned");
+  hipError_t e = attn::launch_clock_probe(reinterpret_cast<unsigned long long*>(out), (long long)spin_us * 100,
+                                          static_cast<hipStream_t>(stream));
+  return hip_status(e, "attn_clock_probe launch");
+}

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 enum {
@@ -317,6 +317,21 @@ int attn_bwd(int dtype, int B, int H, int N, int d,
              const void* o, const float* lse, const void* dout,
              float* delta, void* dq, void* dk, void* dv,
              float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_clock_probe -- measurement aid, not part of the computation: the
+ * shader clock under load.  One wave counts shader cycles against the
+ * 100 MHz real-time counter for spin_us microseconds of real time, so
+ * MHz = out[0] / out[1] * 100.  Launched on a second stream while attention
+ * kernels run, the wave shares a compute unit with them and measures the
+ * clock they run at (it falls well below the 2.4 GHz peak under dense MFMA
+ * work, by the chip's power management).
+ *
+ *   spin_us   1 .. 100000.
+ *   out       device uint64 [2]: shader cycles, real-time ticks.
+ *   stream    hipStream_t or NULL.
+ */
+int attn_clock_probe(int spin_us, uint64_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,10 +35,17 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge",
-                          "attn_bwd", "rope_hadamard_rotate_quant"}
+                          "attn_bwd", "rope_hadamard_rotate_quant", "attn_clock_probe"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
+
+
+@pytest.mark.parametrize("spin,out,msg", [(0, A, "spin_us"), (100001, A, "spin_us"), (10, None, "out is NULL"),
+                                          (10, A + 4, "8-byte aligned")])
+def test_clock_probe_rejections(lib, spin, out, msg):
+    assert lib.attn_clock_probe(spin, out, None) == 1
+    assert msg in lib.attn_last_error().decode()
 
 
 def test_status_strings(lib):
