@@ -1,9 +1,15 @@
 """Builds libattn.so (HIP kernels + C-ABI layer) in-tree for gfx950.
 
-    python -m exact_attention_forward_06_amd.build [--verbose]
+    python -m exact_attention_forward_06_amd.build [--verbose] [--sanitized]
 
 Each source is compiled to an object under <repo>/_build in parallel, then
 linked into exact_attention_forward_06_amd/libattn.so (written atomically).
+
+--sanitized also builds <repo>/_build/san/libattn.so: the same device code
+with the host side of the C-ABI layer (api.cpp: validation, dispatch,
+errors) instrumented by AddressSanitizer and UndefinedBehaviorSanitizer
+(host code only; GPU code is never built with a sanitizer).  Load it with
+the ASan runtime preloaded (asan_runtime()) and ATTN_LIBRARY pointing at it.
 """
 from __future__ import annotations
 
@@ -74,5 +80,55 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_LIB_PATH = os.path.join(SAN_DIR, "libattn.so")
+# host-only sanitizer flags: every -fsanitize sits behind -Xarch_host
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime (to preload into python)."""
+    llvm = os.path.join(os.path.dirname(os.path.dirname(_hipcc())), "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(llvm), reverse=True):
+        cand = os.path.join(llvm, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The host-sanitised variant of libattn.so (see the module docstring);
+    the kernel objects are those of build(), compiled here where missing or
+    older than the sources and headers.  Returns its path."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    newest_header = max(os.path.getmtime(os.path.join(d, f)) for d in (CSRC, os.path.join(ROOT, "include"))
+                        for f in os.listdir(d) if f.endswith(".h"))
+    stale = [src for src in sources() if not src.endswith("api.cpp")
+             and (not os.path.exists(os.path.join(BUILD_DIR, os.path.basename(src) + ".o"))
+                  or os.path.getmtime(os.path.join(BUILD_DIR, os.path.basename(src) + ".o"))
+                  < max(os.path.getmtime(src), newest_header))]
+    if stale:
+        os.makedirs(BUILD_DIR, exist_ok=True)
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(stale))) as ex:
+            list(ex.map(lambda src: _compile(src, verbose), stale))
+    api = os.path.join(CSRC, "api.cpp")
+    obj = os.path.join(SAN_DIR, "api.cpp.o")
+    cmd = [_hipcc(), "-x", "hip", *HIP_FLAGS, "-g", *SAN_FLAGS, "-c", api, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling sanitised api.cpp failed:\n{r.stdout}{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources() if not s.endswith("api.cpp")]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan", *SAN_FLAGS, *objs,
+           "-o", SAN_LIB_PATH]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking the sanitised libattn.so failed:\n{r.stdout}{r.stderr}")
+    return SAN_LIB_PATH
+
+
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose="--verbose" in sys.argv))
+    else:
+        print(build(verbose="--verbose" in sys.argv))
