@@ -15,7 +15,7 @@ Public API (thin wrappers over the C ABI of libattn.so, include/attn.h):
     attn_merge(o_part, lse_part, out_dtype) -> (o, lse)
     attn_bwd(q, k, v, o, lse, dout, causal=False) -> (dq, dk, dv, delta)
 """
-from ._lib import (AttnError, attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_merge, hadamard_rotate_quant,
+from ._lib import (AttnError, attn_bwd, attn_bwd_noalloc, attn_fwd, attn_fwd_fp8, attn_fwd_splitkv, attn_merge, hadamard_rotate_quant,
                    clock_probe, load, rope_hadamard_rotate_quant, splitkv_chunk)
 
 
@@ -37,5 +37,5 @@ def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=No
                         stream=stream, fp8_format=fp8_format)
 
 
-__all__ = ["AttnError", "attn_bwd", "clock_probe", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
+__all__ = ["AttnError", "attn_bwd", "attn_bwd_noalloc", "clock_probe", "attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e2e", "attn_fwd_splitkv", "attn_merge",
            "hadamard_rotate_quant", "load", "rope_hadamard_rotate_quant", "splitkv_chunk"]

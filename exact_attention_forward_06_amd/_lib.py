@@ -42,6 +42,8 @@ _SIGNATURES = {
     "attn_bwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                   ctypes.c_float, _i, _vp], _i),
     "attn_clock_probe": ([_i, _vp, _vp], _i),
+    "attn_bwd_noalloc": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          ctypes.c_float, _i, _vp], _i),
 }
 
 _lib = None
@@ -288,6 +290,37 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, dq=None, d
                         _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)),
                         _stream(stream)))
     return dq, dk, dv, delta
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, softmax_scale=None, stream=None):
+    """attn_bwd through the entry point that allocates nothing: the caller
+    passes the outputs dq, dk, dv (contiguous, dtype of q); the D_i
+    workspace is the library's scratch array (B*H*N <= 2^21).  Calls that
+    overlap on one GPU race on that array."""
+    lib = load()
+    if q.dtype not in _DTYPE_CODE or any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must share a dtype among fp16, bf16")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32")
+    for t in (o, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("attn_bwd_noalloc takes contiguous o, dout and lse")
+    strides = _bhnd_strides(q, k, v)
+    B, H, N, d = q.shape
+    for t in (k, v, o, dout):
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            raise ValueError(f"{name} is required: attn_bwd_noalloc allocates nothing")
+        _buf(t, (B, H, N, d), q.dtype, q.device, name)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_bwd_noalloc(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), _ptr(k), _ptr(v), strides, _ptr(o),
+                                _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)),
+                                _stream(stream)))
+    return dq, dk, dv
 
 
 def clock_probe(spin_us=300, out=None, stream=None):

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -454,10 +455,15 @@ int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_s
 
 }  // extern "C"
 
-extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, const void* k,
-                        const void* v, const int64_t* qkv_strides, const void* o, const float* lse,
-                        const void* dout, float* delta, void* dq, void* dk, void* dv,
-                        float softmax_scale, int causal, void* stream) {
+namespace {
+
+// Validation and argument packing shared by attn_bwd and attn_bwd_noalloc.
+// With scratch_delta the workspace is the library's own array (checked and
+// resolved by the caller after this returns), so delta is not checked here.
+int bwd_prepare(int dtype, int B, int H, int N, int d, const void* q, const void* k, const void* v,
+                const int64_t* qkv_strides, const void* o, const float* lse, const void* dout, float* delta,
+                bool scratch_delta, void* dq, void* dk, void* dv, float softmax_scale, int causal,
+                attn::BwdArgs* a) {
   const int es = elem_size(dtype);
   if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (int st = check_sizes(B, H, N, d)) return st;
@@ -468,14 +474,15 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
   const int64_t tbytes = rows * d * es;
   int64_t sb, sh, sn;
   strides_or_contiguous(qkv_strides, H, N, d, &sb, &sh, &sn);
-  Span sq, sk, sv, so, sl, sdo, sdl, sdq, sdk, sdv;
+  Span sq, sk, sv, so, sl, sdo, sdl = {0, 0}, sdq, sdk, sdv;
   if (int st = check_strided("q", q, B, H, N, d, sb, sh, sn, es, &sq)) return st;
   if (int st = check_strided("k", k, B, H, N, d, sb, sh, sn, es, &sk)) return st;
   if (int st = check_strided("v", v, B, H, N, d, sb, sh, sn, es, &sv)) return st;
   if (int st = check_dense("o", o, tbytes, &so)) return st;
   if (int st = check_dense("lse", lse, rows * 4, &sl, false)) return st;
   if (int st = check_dense("dout", dout, tbytes, &sdo)) return st;
-  if (int st = check_dense("delta", delta, rows * 4, &sdl, false)) return st;
+  if (!scratch_delta)
+    if (int st = check_dense("delta", delta, rows * 4, &sdl, false)) return st;
   if (int st = check_dense("dq", dq, tbytes, &sdq)) return st;
   if (int st = check_dense("dk", dk, tbytes, &sdk)) return st;
   if (int st = check_dense("dv", dv, tbytes, &sdv)) return st;
@@ -492,31 +499,94 @@ extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, co
   if (((int64_t)N + 128) * (sn > d ? sn : d) * es + (int64_t)d * es >= ((int64_t)1 << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
 
-  attn::BwdArgs a;
-  a.dtype = static_cast<attn::Dtype>(dtype);
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  a.d = d;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.sb = sb;
-  a.sh = sh;
-  a.sn = sn;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.delta = delta;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.scale = softmax_scale;
-  a.causal = causal != 0;
+  a->dtype = static_cast<attn::Dtype>(dtype);
+  a->B = B;
+  a->H = H;
+  a->N = N;
+  a->d = d;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->sb = sb;
+  a->sh = sh;
+  a->sn = sn;
+  a->o = o;
+  a->dout = dout;
+  a->lse = lse;
+  a->delta = delta;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->scale = softmax_scale;
+  a->causal = causal != 0;
+  return ATTN_OK;
+}
+
+int bwd_launch(const attn::BwdArgs& a, void* stream) {
   bool supported = true;
   hipError_t e = attn::launch_attn_bwd(a, static_cast<hipStream_t>(stream), &supported);
-  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_bwd kernel for dtype %d d=%d", dtype, d);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_bwd kernel for dtype %d d=%d", (int)a.dtype, a.d);
   return hip_status(e, "attn_bwd launch");
+}
+
+// The workspace of attn_bwd_noalloc: one array per GPU, in the library's
+// device code object, alive until the process ends.  Host code must never
+// pass `scratch` itself to a kernel (in host code the name is a stand-in,
+// not a device address): its per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchFloats = (int64_t)1 << 21;   // 8 MiB: delta of up to 2^21 rows
+__device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array (resolved on the first call on
+// the current device).
+int scratch_address(float** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "device %d is beyond the %d the scratch table covers", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)))
+      return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(int dtype, int B, int H, int N, int d, const void* q, const void* k,
+                        const void* v, const int64_t* qkv_strides, const void* o, const float* lse,
+                        const void* dout, float* delta, void* dq, void* dk, void* dv,
+                        float softmax_scale, int causal, void* stream) {
+  attn::BwdArgs a;
+  if (int st = bwd_prepare(dtype, B, H, N, d, q, k, v, qkv_strides, o, lse, dout, delta, false, dq, dk, dv,
+                           softmax_scale, causal, &a))
+    return st;
+  return bwd_launch(a, stream);
+}
+
+extern "C" int attn_bwd_noalloc(int dtype, int B, int H, int N, int d, const void* q, const void* k,
+                                const void* v, const int64_t* qkv_strides, const void* o, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, float softmax_scale,
+                                int causal, void* stream) {
+  attn::BwdArgs a;
+  if (int st = bwd_prepare(dtype, B, H, N, d, q, k, v, qkv_strides, o, lse, dout, nullptr, true, dq, dk, dv,
+                           softmax_scale, causal, &a))
+    return st;
+  if ((int64_t)B * H * N > kScratchFloats)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "B*H*N = %lld rows exceed the %lld of the library's scratch array",
+                (long long)B * H * N, (long long)kScratchFloats);
+  float* delta = nullptr;
+  if (int st = scratch_address(&delta)) return st;
+  a.delta = delta;
+  return bwd_launch(a, stream);
 }
 
 extern "C" int attn_clock_probe(int spin_us, uint64_t* out, void* stream) {

@@ -319,6 +319,31 @@ int attn_bwd(int dtype, int B, int H, int N, int d,
              float softmax_scale, int causal, void* stream);
 
 /*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and arguments without `delta`,
+ * whose role (D_i = dO_i . O_i, fp32 [B, H, N]) is taken by the library's
+ * own scratch array, a file-scope device array of 2^21 floats (8 MiB) per
+ * GPU that lives until the process ends.
+ *
+ *   Arguments as attn_bwd; B * H * N must not exceed 2^21 (2,097,152 rows),
+ *   or the call fails with ATTN_ERR_INVALID_ARGUMENT before any HIP call.
+ *
+ * The call allocates nothing (no hipMalloc, no library allocation); on the
+ * first call on a device it looks up that device's scratch address
+ * (hipGetSymbolAddress) and keeps it.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, or two
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * array needs clearing: the first launch writes every D_i the second reads.
+ */
+int attn_bwd_noalloc(int dtype, int B, int H, int N, int d,
+                     const void* q, const void* k, const void* v,
+                     const int64_t* qkv_strides,
+                     const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv,
+                     float softmax_scale, int causal, void* stream);
+
+/*
  * attn_clock_probe -- measurement aid, not part of the computation: the
  * shader clock under load.  One wave counts shader cycles against the
  * 100 MHz real-time counter for spin_us microseconds of real time, so

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge",
-                          "attn_bwd", "rope_hadamard_rotate_quant", "attn_clock_probe"}
+                          "attn_bwd", "rope_hadamard_rotate_quant", "attn_clock_probe", "attn_bwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_abi_version() == 5
