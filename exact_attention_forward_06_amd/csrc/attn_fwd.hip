@@ -171,7 +171,7 @@ void attn_fwd16_kernel(Params p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;   // running max of scale * log2(e) * s (possibly stale by < kTau)
+  float m_run = -INFINITY;   // whole-number running max of scale * log2(e) * s (possibly stale by < kTau)
   float l_run = 0.f;         // this lane's half of the running row sum
 
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
@@ -217,8 +217,11 @@ void attn_fwd16_kernel(Params p) {
   // more than kTau (then P = exp2(s c - m_run) <= 2^kTau)
   auto update_max = [&](float m_tile) __attribute__((always_inline)) {
     if (__any(m_tile > m_run + kTau)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      // whole numbers: the rescale is an exact power of two, and P is rounded
+      // to 16 bits on a grid that does not depend on where the running max
+      // happened to lie (so other tilings of the keys round P identically)
+      const float m_new = ceilf(fmaxf(m_run, m_tile));
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - m_new));
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)

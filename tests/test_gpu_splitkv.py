@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_06_amd import attn_fwd_splitkv, attn_merge, splitkv_chunk
+from exact_attention_forward_06_amd import attn_fwd, attn_fwd_splitkv, attn_merge, splitkv_chunk
 from exact_attention_forward_06_amd.inputs import make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +108,43 @@ def test_merge_matches_oracle(d, out):
         np.testing.assert_allclose(og, o_ref, rtol=1e-5, atol=1e-5)
     else:
         np.testing.assert_allclose(og, o_ref, rtol=2 ** -8, atol=1e-3)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_two_tilings_agree(dtype, d, causal):
+    """Two tilings of one computation: attn_fwd (one pass over every K/V
+    tile, one running max and sum) and attn_fwd_splitkv with 2 and 3 key
+    ranges (a pass per range, each normalised on its own, merged through
+    the LSEs in fp32).  Both accumulate in fp32 and round O once, so they
+    must agree to within that rounding: at most 0.1 % of the elements more
+    than one ulp of the 16-bit type apart, none by more than one ulp plus
+    2^-8 max|V| (a weight rounded to the neighbouring 16-bit value moves its
+    row by at most 2^-8 of |V_j - O_i|), and the LSE to fp32 precision.  Both round P to 16 bits against a whole-number
+    running max, so P's rounding grid is the same whatever the tiling; what
+    remains is the fp32 rounding of the exponent s c - m, whose m differs
+    between the tilings, which flips the rounding of the rare weight that
+    lies within ~1e-6 of a midpoint (a dominant one moves its row by up to
+    two ulps).  A race or a tile-order
+    dependence in either kernel breaks this without any oracle involved."""
+    B, H, N = 2, 3, 1000
+    print(f"two tilings {dtype} d={d} causal={causal}", flush=True)
+    inp = make_inputs(B, H, N, d, dtype, seed=23 + d)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o1, l1 = attn_fwd(q, k, v, causal=causal)
+    mant = 7 if dtype == "bf16" else 10
+    for splits in (2, 3):
+        o2, l2, _, _ = attn_fwd_splitkv(q, k, v, splits, causal=causal)
+        torch.cuda.synchronize()
+        a, b = o1.double(), o2.double()
+        big = torch.maximum(a.abs(), b.abs()).clamp_min(2.0 ** -60)
+        ulp = torch.exp2(torch.floor(torch.log2(big)) - mant)
+        diff = (a - b).abs()
+        over1 = (diff > ulp + 2.0 ** -20).double().mean().item()
+        print(f"  splits={splits}: beyond 1 ulp {over1:.2e} of the elements, max {diff.max().item():.3e}", flush=True)
+        vmax = v.abs().max().double().item()
+        assert (diff <= ulp + 2.0 ** -8 * vmax).all(), f"splits={splits}: an element differs beyond one flipped weight"
+        assert over1 <= 1e-3, f"splits={splits}: {over1:.2e} of the elements differ by more than 1 ulp"
+        assert (diff > 0).double().mean().item() < 0.1, "the two tilings differ on many elements"
+        assert (l1.double() - l2.double()).abs().max().item() <= 1e-5
