@@ -5,6 +5,11 @@
 Each source is compiled to an object under <repo>/_build in parallel, then
 linked into exact_attention_forward_06_amd/libattn.so (written atomically).
 
+--poison also builds exact_attention_forward_06_amd/libattn_poison.so: a
+debug build (ATTN_LDS_POISON) whose K/V tile copies first fill their LDS
+destination with NaN, so a stage read before its copy has landed shows up as
+NaN in the output; run the parity tests against it with ATTN_LIBRARY.
+
 --sanitized also builds <repo>/_build/san/libattn.so: the same device code
 with the host side of the C-ABI layer (api.cpp: validation, dispatch,
 errors) instrumented by AddressSanitizer and UndefinedBehaviorSanitizer
@@ -127,8 +132,40 @@ def build_sanitized(verbose: bool = False) -> str:
     return SAN_LIB_PATH
 
 
+POISON_LIB_PATH = os.path.join(PKG_DIR, "libattn_poison.so")
+
+
+def build_poison(verbose: bool = False) -> str:
+    """The LDS-poison debug build (see the module docstring).  Returns its path."""
+    odir = os.path.join(BUILD_DIR, "poison")
+    os.makedirs(odir, exist_ok=True)
+
+    def comp(src):
+        obj = os.path.join(odir, os.path.basename(src) + ".o")
+        cmd = [_hipcc(), *HIP_FLAGS, "-DATTN_LDS_POISON=1", "-c", src, "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compiling {os.path.basename(src)} (poison) failed:\n{r.stdout}{r.stderr}")
+        return obj
+
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    tmp = POISON_LIB_PATH + ".tmp"
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking libattn_poison.so failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, POISON_LIB_PATH)
+    return POISON_LIB_PATH
+
+
 if __name__ == "__main__":
-    if "--sanitized" in sys.argv:
+    if "--poison" in sys.argv:
+        print(build_poison(verbose="--verbose" in sys.argv))
+    elif "--sanitized" in sys.argv:
         print(build_sanitized(verbose="--verbose" in sys.argv))
     else:
         print(build(verbose="--verbose" in sys.argv))

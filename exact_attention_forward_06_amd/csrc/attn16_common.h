@@ -85,8 +85,19 @@ __device__ __forceinline__ int swz(int row) {
 // to the tile's first row and `base` (wave-uniform, the buffer's scalar
 // offset) that row's offset.  (A free function: lambdas inside the kernel
 // must not capture buffer descriptors, or the host pass drops the kernel.)
+// Debug builds with ATTN_LDS_POISON fill every 16 bytes a copy is about to
+// land in with NaN first (and wait for those writes), so a read of a stage
+// before its copy has landed -- a missing wait or barrier -- turns into NaN
+// in the output instead of stale but plausible values.
 template <int LOADS, int NT>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int wave, int base, const int* off) {
+#ifdef ATTN_LDS_POISON
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t)
+    *(__attribute__((address_space(3))) u32x4_t*)(dst + (t * NT + wave * 64 + (int)(threadIdx.x & 63)) * 16) =
+        u32x4_t{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the NaN writes have landed
+#endif
 #pragma unroll
   for (int t = 0; t < LOADS; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (t * NT + wave * 64) * 16), 16, off[t], base, 0, 0);

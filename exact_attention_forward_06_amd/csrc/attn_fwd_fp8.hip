@@ -125,8 +125,17 @@ __device__ __forceinline__ int swz_v(int row) {
 // Global -> LDS copy of one tile of ROWS x RB bytes (row pitch `pitch` in
 // global memory) into `dst`; DMA instruction t of a wave writes LDS bytes
 // [(t * NT + wave * 64) * 16, + 1024), lane l at + 16 l.
+// Debug builds with ATTN_LDS_POISON fill the destination with E4M3 NaN
+// codes (0x7F) first, so a read before the copy has landed shows as NaN.
 template <int LOADS, int NT>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, char* dst, int wave, int base, const int* off) {
+#ifdef ATTN_LDS_POISON
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t)
+    *(lds_u32x4_t*)(dst + (t * NT + wave * 64 + (int)(threadIdx.x & 63)) * 16) =
+        u32x4_t{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the NaN writes have landed
+#endif
 #pragma unroll
   for (int t = 0; t < LOADS; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (t * NT + wave * 64) * 16), 16, off[t], base,
