@@ -20,12 +20,22 @@ from ._lib import (AttnError, attn_bwd, attn_bwd_noalloc, attn_fwd, attn_fwd_fp8
 
 
 def attn_fwd_fp8_e2e(q, k, v, signs, causal=False, softmax_scale=None, stream=None, fp8_format="e4m3",
-                     rope=None):
+                     rope=None, per_tensor=False):
     """The whole FP8 path: rotate+quantise Q and K with the shared signs,
     quantise V into the transposed layout, then the FP8 attention kernel
     (codes in fp8_format: "e4m3" or "e5m2").  rope = dict(style=..., base=...,
     pos_offset=...) puts RoPE in front of the rotation of Q and K (one fused
-    pass each)."""
+    pass each).  per_tensor=True quantises with one scale per (b, h) instead
+    of per 128-row block (not with rope)."""
+    if per_tensor:
+        if rope is not None:
+            raise ValueError("per_tensor scales are not combined with rope")
+        q8, sq = hadamard_rotate_quant(q, signs, stream=stream, fp8_format=fp8_format, per_tensor=True)
+        k8, sk = hadamard_rotate_quant(k, signs, stream=stream, fp8_format=fp8_format, per_tensor=True)
+        v8t, sv = hadamard_rotate_quant(v, None, transpose_out=True, stream=stream, fp8_format=fp8_format,
+                                        per_tensor=True)
+        return attn_fwd_fp8(q8, sq, k8, sk, v8t, sv, causal=causal, softmax_scale=softmax_scale,
+                            stream=stream, fp8_format=fp8_format)
     if rope is None:
         q8, sq = hadamard_rotate_quant(q, signs, stream=stream, fp8_format=fp8_format)
         k8, sk = hadamard_rotate_quant(k, signs, stream=stream, fp8_format=fp8_format)

@@ -32,6 +32,7 @@ _SIGNATURES = {
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_fwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i, _vp], _i),
     "hadamard_rotate_quant": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
+    "hadamard_rotate_quant_per_tensor": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "attn_fwd_fp8": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, ctypes.c_float,
                       _i, _vp], _i),
     "attn_fwd_splitkv": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
@@ -185,10 +186,11 @@ def attn_merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None, s
 
 
 def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, out=None,
-                          scales=None, stream=None, fp8_format="e4m3"):
+                          scales=None, stream=None, fp8_format="e4m3", per_tensor=False):
     """FP8 pre-pass of one [B, H, N, d] tensor: optional rotation by
     (1/sqrt(d)) H diag(signs), per-block amax scale and codes in fp8_format
-    ("e4m3" or "e5m2").
+    ("e4m3" or "e5m2"); per_tensor=True takes one scale per (b, h) instead
+    (hadamard_rotate_quant_per_tensor: every slot of a head holds it).
     Returns (codes uint8 [B,H,N,d] or [B,H,d,N], scales fp32 [B,H,nblk])."""
     lib = load()
     if x.dtype not in _DTYPE_CODE:
@@ -199,9 +201,9 @@ def hadamard_rotate_quant(x, signs=None, block_rows=128, transpose_out=False, ou
     out = _buf(out, (B, H, d, N) if transpose_out else (B, H, N, d), torch.uint8, x.device, "out")
     scales = _buf(scales, (B, H, nblk), torch.float32, x.device, "scales")
     _check_signs(signs, d)
-    _check(lib.hadamard_rotate_quant(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides,
-                                     _ptr(signs), block_rows, FP8_FORMATS[fp8_format],
-                                     int(bool(transpose_out)), _ptr(out), _ptr(scales), _stream(stream)))
+    fn = lib.hadamard_rotate_quant_per_tensor if per_tensor else lib.hadamard_rotate_quant
+    _check(fn(_DTYPE_CODE[x.dtype], B, H, N, d, _ptr(x), strides, _ptr(signs), block_rows,
+              FP8_FORMATS[fp8_format], int(bool(transpose_out)), _ptr(out), _ptr(scales), _stream(stream)))
     return out, scales
 
 

@@ -294,10 +294,13 @@ int attn_merge(int out_dtype, int S, int B, int H, int N, int d, const float* o_
   return hip_status(e, "attn_merge launch");
 }
 
-int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,
-                          const int64_t* x_strides, const int8_t* signs, int block_rows,
-                          int fp8_format, int transpose_out, uint8_t* x8, float* scales,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+int rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x, const int64_t* x_strides,
+                 const int8_t* signs, int block_rows, int fp8_format, int transpose_out, uint8_t* x8,
+                 float* scales, void* stream, bool per_head) {
   const int es = elem_size(in_dtype);
   if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", in_dtype);
   if (int st = check_sizes(B, H, N, d)) return st;
@@ -337,10 +340,31 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* 
   a.transpose_out = transpose_out != 0;
   a.x8 = x8;
   a.scales = scales;
+  a.per_head = per_head;
   bool supported = true;
   hipError_t e = attn::launch_hadamard_rotate_quant(a, static_cast<hipStream_t>(stream), &supported);
   if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no hadamard_rotate_quant kernel for d=%d", d);
   return hip_status(e, "hadamard_rotate_quant launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,
+                          const int64_t* x_strides, const int8_t* signs, int block_rows,
+                          int fp8_format, int transpose_out, uint8_t* x8, float* scales,
+                          void* stream) {
+  return rotate_quant(in_dtype, B, H, N, d, x, x_strides, signs, block_rows, fp8_format, transpose_out, x8,
+                      scales, stream, false);
+}
+
+int hadamard_rotate_quant_per_tensor(int in_dtype, int B, int H, int N, int d, const void* x,
+                                     const int64_t* x_strides, const int8_t* signs, int block_rows,
+                                     int fp8_format, int transpose_out, uint8_t* x8, float* scales,
+                                     void* stream) {
+  return rotate_quant(in_dtype, B, H, N, d, x, x_strides, signs, block_rows, fp8_format, transpose_out, x8,
+                      scales, stream, true);
 }
 
 int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d, const void* x,

@@ -30,6 +30,12 @@
 //    share the significand 1.75, so the quotient stays exact alike.
 //  * transpose_out writes [d][n] (the layout the FP8 attention kernel wants
 //    for V): codes are transposed through LDS so global stores stay 16-byte.
+//  * Per-head scales (the coarser granularity the per-block scheme is
+//    compared with: one scale per (b, h) instead of per 128 rows) run in
+//    three launches: block amaxes into the scale slots, their maximum per
+//    head into every slot, then the codes with the head's amax; x is read
+//    twice, and the [B, H, N/128] scale array the attention kernel reads
+//    holds the head's scale in every slot.
 //  * RoPE (ROPE = 1: pairs (2i, 2i+1); ROPE = 2: pairs (i, i + d/2)) runs on
 //    the loaded fp32 values before D and H, so the producer pass that the
 //    "FlashAttention-3" page suggests (Hadamard fused with a bandwidth-bound
@@ -138,7 +144,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-template <typename T, int D, bool ROT, bool TRANS, int FMT, int ROPE = 0>
+// PT: 0 = one scale per 128-row block; per-head scales in two passes around
+// head_amax_kernel: 1 = write the block's amax into its scale slot and stop,
+// 2 = quantise with the amax found in the slot (the head's) and overwrite
+// the slot with the head's scale.
+template <typename T, int D, bool ROT, bool TRANS, int FMT, int ROPE = 0, int PT = 0>
 __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p, typename RopeArg<ROPE>::type rt) {
   static_assert(!(ROPE && TRANS), "RoPE applies to Q and K, which are not transposed");
   constexpr float QMAX = FMT == 0 ? 448.f : 57344.f;   // largest finite E4M3 / E5M2 value
@@ -239,16 +249,24 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p, typename 
   }
 
   // block amax
+  float* slot = p.scales + (int64_t)bh * p.nblk + blk;
+  float head_amax = 0.f;
+  if constexpr (PT == 2) head_amax = *slot;   // read before the barrier after which thread 0 rewrites it
   amax = wave_max(amax);
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if constexpr (PT == 1) {
+    if (tid == 0) *slot = amax;
+    return;
+  }
+  if constexpr (PT == 2) amax = head_amax;
   // y = (x~ * 448) / amax, formed as a product with 1/amax plus one FMA
   // remainder correction: the remainder a - y0 * amax is exact in an FMA,
   // so a quotient that is representable (e.g. an exact E4M3 rounding tie,
   // frequent for 16-bit inputs whose x * 448 is exact) comes out exactly.
   const float ramax = amax > 0.f ? 1.f / amax : 0.f;
-  if (tid == 0) p.scales[(int64_t)bh * p.nblk + blk] = amax * p.scale_norm / QMAX;   // 0 for a zero block
+  if (tid == 0) *slot = amax * p.scale_norm / QMAX;   // 0 for a zero block
 
   // codes
   uint8_t* out = p.x8 + (int64_t)bh * p.N * D;
@@ -304,6 +322,30 @@ __global__ __launch_bounds__(NT) void hadamard_quant_kernel(QParams p, typename 
   }
 }
 
+// Per-head amax: one workgroup per (b, h) reads the head's block amaxes from
+// its scale slots and writes their maximum back to every slot.
+__global__ __launch_bounds__(NT) void head_amax_kernel(float* scales, int nblk) {
+  __shared__ float red[NT / 64];
+  float* s = scales + (int64_t)blockIdx.x * nblk;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < nblk; i += NT) m = fmaxf(m, s[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  for (int i = threadIdx.x; i < nblk; i += NT) s[i] = m;
+}
+
+template <typename T, int D, bool ROT, bool TRANS, int FMT>
+hipError_t launch_per_head(const QParams& p, int bh_count, hipStream_t s) {
+  const NoRope nr{0};
+  dim3 grid(p.nblk, bh_count);
+  hipLaunchKernelGGL((hadamard_quant_kernel<T, D, ROT, TRANS, FMT, 0, 1>), grid, dim3(NT), 0, s, p, nr);
+  hipLaunchKernelGGL(head_amax_kernel, dim3(bh_count), dim3(NT), 0, s, p.scales, p.nblk);
+  hipLaunchKernelGGL((hadamard_quant_kernel<T, D, ROT, TRANS, FMT, 0, 2>), grid, dim3(NT), 0, s, p, nr);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int FMT>
 hipError_t launch_f(const QuantArgs& a, hipStream_t s) {
   QParams p;
@@ -319,6 +361,12 @@ hipError_t launch_f(const QuantArgs& a, hipStream_t s) {
   p.nblk = (a.N + ROWS - 1) / ROWS;
   p.scale_norm = a.signs ? 1.f / sqrtf((float)D) : 1.f;
   dim3 grid(p.nblk, a.B * a.H);
+  if (a.per_head) {
+    if (a.signs) return a.transpose_out ? launch_per_head<T, D, true, true, FMT>(p, a.B * a.H, s)
+                                        : launch_per_head<T, D, true, false, FMT>(p, a.B * a.H, s);
+    return a.transpose_out ? launch_per_head<T, D, false, true, FMT>(p, a.B * a.H, s)
+                           : launch_per_head<T, D, false, false, FMT>(p, a.B * a.H, s);
+  }
   if (a.rope_style != 0) {
     RopeTab rt;
     for (int i = 0; i < D / 2; ++i) rt.theta[i] = pow(a.rope_base, -2.0 * i / D);
@@ -365,7 +413,7 @@ hipError_t launch_t(const QuantArgs& a, hipStream_t s, bool* ok) {
 
 hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported) {
   if (a.block_rows != ROWS || (a.fp8_format != 0 && a.fp8_format != 1) || a.rope_style < 0 || a.rope_style > 2 ||
-      (a.rope_style != 0 && a.transpose_out)) {
+      (a.rope_style != 0 && a.transpose_out) || (a.per_head && a.rope_style != 0)) {
     *supported = false;
     return hipSuccess;
   }

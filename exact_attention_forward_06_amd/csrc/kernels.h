@@ -50,6 +50,7 @@ struct QuantArgs {
   int rope_style = 0;
   double rope_base = 10000.0;
   int pos_offset = 0;   // position of row 0
+  bool per_head = false;   // one scale per (b, h), replicated into every 128-row slot
 };
 
 struct Fp8FwdArgs {

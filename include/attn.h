@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 /* Status codes returned by every entry point. */
 enum {
@@ -203,6 +203,27 @@ int hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
                           const int8_t* signs, int block_rows, int fp8_format,
                           int transpose_out, uint8_t* x8, float* scales,
                           void* stream);
+
+/*
+ * hadamard_rotate_quant_per_tensor -- the same pre-pass with one scale per
+ * (b, h) instead of per block of 128 rows: the coarser granularity that
+ * per-block quantisation ("FlashAttention-2/3" page, FlashAttention-3 特性三)
+ * is compared with.  amax = max |x~| over all N rows of the head, and the
+ * codes follow the rule of hadamard_rotate_quant with that amax.
+ *
+ *   Arguments as hadamard_rotate_quant (block_rows must be 128).  scales is
+ *   still [B, H, ceil(N / block_rows)], every slot of a head holding the
+ *   head's scale, so attn_fwd_fp8 consumes the codes unchanged.
+ *
+ * Three launches on `stream`: the block amaxes into the scale slots, their
+ * maximum per head into every slot, then the codes (x is read twice); the
+ * scale array is the only intermediate storage.
+ */
+int hadamard_rotate_quant_per_tensor(int in_dtype, int B, int H, int N, int d,
+                                     const void* x, const int64_t* x_strides,
+                                     const int8_t* signs, int block_rows, int fp8_format,
+                                     int transpose_out, uint8_t* x8, float* scales,
+                                     void* stream);
 
 /*
  * attn_fwd_fp8 -- attention forward on FP8 codes with per-block scales.

@@ -35,10 +35,11 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge",
-                          "attn_bwd", "rope_hadamard_rotate_quant", "attn_clock_probe", "attn_bwd_noalloc"}
+                          "attn_bwd", "rope_hadamard_rotate_quant", "attn_clock_probe", "attn_bwd_noalloc",
+                          "hadamard_rotate_quant_per_tensor"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
 
 
 @pytest.mark.parametrize("spin,out,msg", [(0, A, "spin_us"), (100001, A, "spin_us"), (10, None, "out is NULL"),
@@ -93,9 +94,10 @@ def test_attn_fwd_rejects(lib, kw, status, msg):
 
 
 def _quant(lib, dtype=2, B=1, H=1, N=256, d=128, x=A, strides=None, signs=B_, block_rows=128,
-           fmt=0, t=0, x8=O, sc=L):
+           fmt=0, t=0, x8=O, sc=L, per_tensor=False):
     s = None if strides is None else (ctypes.c_int64 * 3)(*strides)
-    return lib.hadamard_rotate_quant(dtype, B, H, N, d, x, s, signs, block_rows, fmt, t, x8, sc, None)
+    fn = lib.hadamard_rotate_quant_per_tensor if per_tensor else lib.hadamard_rotate_quant
+    return fn(dtype, B, H, N, d, x, s, signs, block_rows, fmt, t, x8, sc, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -111,8 +113,9 @@ def _quant(lib, dtype=2, B=1, H=1, N=256, d=128, x=A, strides=None, signs=B_, bl
     (dict(fmt=2), 1, "fp8_format"),
     (dict(fmt=-1), 1, "fp8_format"),
 ])
-def test_quant_rejects(lib, kw, status, msg):
-    assert _quant(lib, **kw) == status
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_quant_rejects(lib, kw, status, msg, per_tensor):
+    assert _quant(lib, per_tensor=per_tensor, **kw) == status
     assert msg in lib.attn_last_error().decode()
 
 

@@ -106,6 +106,47 @@ def test_hadamard_rotate_quant_parity(dtype, d, rot, trans, fmt):
         assert flips == 0, "16-bit inputs without rotation must give the oracle's codes exactly"
 
 
+@pytest.mark.parametrize("rot,trans", [(True, False), (False, True), (False, False)])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("N", [300, 512])
+def test_per_tensor_quant_parity(d, rot, trans, N):
+    """hadamard_rotate_quant_per_tensor: one scale per (b, h) over all N rows
+    (the oracle's block quantisation with block_rows = N), replicated into
+    every 128-row slot; codes as in the per-block test."""
+    if trans and N % 16:
+        pytest.skip("transposed output needs N % 16 == 0")
+    inp = make_inputs(2, 3, N, d, "bf16", seed=d + N + 5)
+    x = inp["q"]
+    x[..., 3] *= 20
+    x[0, 1, 7:9] *= 4                     # one head with a larger maximum elsewhere
+    signs = random_signs(d, seed=d + 1) if rot else None
+    codes, scales = hadamard_rotate_quant(x.cuda(), None if signs is None else signs.cuda(), transpose_out=trans,
+                                          per_tensor=True)
+    torch.cuda.synchronize()
+    c_ref, s_ref, y_ref = oracle.hadamard_rotate_quant(to_f64(x), None if signs is None else signs.numpy(), N,
+                                                       transpose_out=trans)
+    sc = scales.cpu().double().numpy()
+    assert sc.shape == (2, 3, -(-N // 128))
+    np.testing.assert_allclose(sc, np.broadcast_to(s_ref, sc.shape), rtol=2e-6)
+    flips = _codes_match(codes.cpu().numpy(), c_ref, y_ref, _band(y_ref, d, rot), f"per-tensor d={d} rot={rot}")
+    if not rot:
+        assert flips == 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_per_tensor_attention_matches_simulation(d, causal):
+    B, H, N = 1, 2, 512
+    inp = _fp8_inputs(B, H, N, d, seed=d + 71, outliers=True)
+    o, lse = attn_fwd_fp8_e2e(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["signs"].cuda(),
+                              causal=causal, per_tensor=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fp8_simulated(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]),
+                                                    inp["signs"].numpy(), 1 / math.sqrt(d), causal, block_rows=N,
+                                                    quantize_p=True, p_block=p_block(d))
+    _check_sim(o, lse, o_ref, lse_ref, f"per-tensor d={d} causal={causal}")
+
+
 def test_hadamard_block_max_encodes_to_448():
     inp = make_inputs(1, 2, 256, 128, "bf16", seed=3)
     signs = random_signs(128, 3)
@@ -323,35 +364,39 @@ def test_fp8_workload_full(rotated, capsys):
 def test_fp8_outlier_sweep_rotation_on_gpu(capsys):
     """The GPU FP8 path against exact attention with and without the
     rotation, over outlier-channel rates 0, 0.5, 2 and 5 % of d (x20; 0, 1, 3
-    and 6 channels at d = 128).  With three or more outlier channels the
-    rotation must lower the error at least two-fold (the direction of the
-    pages' "about 2.6x" claim, "FlashAttention-3" page, section "FP8 路径与低
-    精度误差"); with none it changes little.  A single outlier channel is
-    reported only: whether it hurts the unrotated codes depends on the draw
-    (the oracle's simulation shows both directions across seeds)."""
+    and 6 channels at d = 128), with per-block (128 rows) and per-tensor (one
+    per (b, h)) scales.  With three or more outlier channels the rotation
+    must lower the error at least two-fold at both granularities (the
+    direction of the pages' "about 2.6x" claim, "FlashAttention-3" page,
+    section "FP8 路径与低精度误差"); with none it changes little.  A single
+    outlier channel is reported only: whether it hurts the unrotated codes
+    depends on the draw (the oracle's simulation shows both directions across
+    seeds)."""
     B, H, N, d = 1, 4, 1024, 128
     rows = []
     for frac in (0.0, 0.005, 0.02, 0.05):
         inp = make_inputs(B, H, N, d, "fp8", seed=11, outlier_frac=frac)
         q, k, v, sg = (inp[n].cuda() for n in ("q", "k", "v", "signs"))
-        o_rot, _ = attn_fwd_fp8_e2e(q, k, v, sg)
-        q8, sq = hadamard_rotate_quant(q, None)
-        k8, sk = hadamard_rotate_quant(k, None)
-        v8, sv = hadamard_rotate_quant(v, None, transpose_out=True)
-        o_plain, _ = attn_fwd_fp8(q8, sq, k8, sk, v8, sv)
-        torch.cuda.synchronize()
         exact, _ = oracle.attention(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), 1 / math.sqrt(d))
-        e_rot = oracle.rel_rms(to_f64(o_rot.cpu()), exact)
-        e_plain = oracle.rel_rms(to_f64(o_plain.cpu()), exact)
-        rows.append((frac, e_rot, e_plain))
-        assert math.isfinite(e_rot) and math.isfinite(e_plain)
-        if frac == 0.0:
-            assert 0.8 <= e_plain / e_rot <= 1.25, (frac, e_rot, e_plain)
-        elif frac >= 0.02:
-            assert e_plain / e_rot >= 2.0, (frac, e_rot, e_plain)
+        res = {}
+        for per_tensor in (False, True):
+            o_rot, _ = attn_fwd_fp8_e2e(q, k, v, sg, per_tensor=per_tensor)
+            o_plain, _ = attn_fwd_fp8_e2e(q, k, v, None, per_tensor=per_tensor)
+            torch.cuda.synchronize()
+            e_rot = oracle.rel_rms(to_f64(o_rot.cpu()), exact)
+            e_plain = oracle.rel_rms(to_f64(o_plain.cpu()), exact)
+            res[per_tensor] = (e_rot, e_plain)
+            assert math.isfinite(e_rot) and math.isfinite(e_plain)
+            if frac == 0.0:
+                assert 0.8 <= e_plain / e_rot <= 1.25, (frac, per_tensor, e_rot, e_plain)
+            elif frac >= 0.02:
+                assert e_plain / e_rot >= 2.0, (frac, per_tensor, e_rot, e_plain)
+        rows.append((frac, res))
     with capsys.disabled():
-        print("\n[fp8 outlier sweep] rel RMS vs exact (rotated / unrotated / ratio): " +
-              "; ".join(f"{f * 100:.1f}%: {r:.4f} / {p:.4f} / {p / r:.2f}x" for f, r, p in rows), flush=True)
+        print("\n[fp8 outlier sweep] rel RMS vs exact, rotated / unrotated / ratio, per-block | per-tensor: " +
+              "; ".join(f"{f * 100:.1f}%: {r[False][0]:.4f} / {r[False][1]:.4f} / {r[False][1] / r[False][0]:.2f}x | "
+                        f"{r[True][0]:.4f} / {r[True][1]:.4f} / {r[True][1] / r[True][0]:.2f}x" for f, r in rows),
+              flush=True)
 
 
 def test_fp8_e5m2_error_exceeds_e4m3(capsys):
