@@ -194,8 +194,8 @@ int attn_fwd_splitkv(int dtype, int B, int H, int N, int d, const void* q, const
   if (int st = check_scale_causal(softmax_scale, causal)) return st;
   if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "num_splits must be in 1..%d", ATTN_MAX_SPLITS);
-  if (dtype == ATTN_F32 || d == 256)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv covers fp16 / bf16 with d = 64 or 128");
+  if (dtype == ATTN_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv covers fp16 / bf16");
   int64_t sb, sh, sn;
   strides_or_contiguous(qkv_strides, H, N, d, &sb, &sh, &sn);
   const int64_t rows = (int64_t)B * H * N;
@@ -253,7 +253,8 @@ int attn_fwd_splitkv(int dtype, int B, int H, int N, int d, const void* q, const
   m.lse = lse;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   bool supported = true;
-  hipError_t e = attn::launch_attn_fwd16_pp_split(a, hs, &supported);
+  hipError_t e = d == 256 ? attn::launch_attn_fwd16_pair_split(a, hs, &supported)
+                          : attn::launch_attn_fwd16_pp_split(a, hs, &supported);
   if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no split-KV kernel for dtype %d d=%d", dtype, d);
   if (e != hipSuccess) return hip_status(e, "attn_fwd_splitkv launch");
   e = attn::launch_attn_merge(m, hs, &supported);

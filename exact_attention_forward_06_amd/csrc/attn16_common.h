@@ -1,5 +1,6 @@
-// Pieces shared by the attention forward kernels (the 16-bit attn_fwd.hip
-// and attn_fwd_pp.hip, and the fp32 attn_fwd_f32.hip): kernel parameters,
+// Pieces shared by the attention kernels (the 16-bit forward kernels of
+// attn_fwd_pp.hip and attn_fwd_pair.hip, the backward attn_bwd.hip and the
+// fp32 forward attn_fwd_f32.hip): kernel parameters,
 // the MFMA / rounding wrappers, the key permutation of the S^T accumulator,
 // the LDS swizzle and the global -> LDS tile copy.  Private to those
 // translation units.

@@ -1,5 +1,5 @@
 // Exact-attention forward for gfx950, fp32 inputs (the 16-bit types have
-// their own kernels in attn_fwd_pp.hip and attn_fwd.hip): fp32 MFMA and
+// their own kernels in attn_fwd_pp.hip and attn_fwd_pair.hip): fp32 MFMA and
 // accumulation, causal or non-causal, per-row logsumexp output.
 //
 // Method (see include/attn.h for the sources on the pages): the grid runs

@@ -8,7 +8,7 @@
 // as in the FP8 path of the "FlashAttention-3" page (section
 // "FP8 路径与低精度误差") with per-block quantisation ("FlashAttention-2/3"
 // page, FlashAttention-3 特性三); the online softmax is that of the 16-bit
-// kernel (attn_fwd.hip), whose layout choices it shares.
+// kernels (attn_fwd_pp.hip), whose layout choices it shares.
 //
 //  * S: one 32x32x64 MFMA per 64 of d.  128-row workgroups and 64-key tiles
 //    never straddle a 128-row scale block, so sQ * sK * softmax_scale *
@@ -387,15 +387,6 @@ void attn_fwd_fp8_kernel(F8Params p) {
 // unit accepts it (about 256 cycles for a 32 KiB pair), which the MFMA phase
 // absorbs in its wait at the barrier.
 
-__device__ __forceinline__ void phase_barrier8() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int V>
-using ic8 = std::integral_constant<int, V>;
-
 template <int D, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_pp_kernel(F8Params p) {
@@ -643,7 +634,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
       constexpr int TM = decltype(tm_c)::value;
       if constexpr ((TM & 1) == 0 && G == 0) {
         const int j = t / 2 + 1;
-        if (j <= n_tiles) copy_pair(j, ic8<(TM == 0) ? 1 : 0>{});
+        if (j <= n_tiles) copy_pair(j, ic<(TM == 0) ? 1 : 0>{});
       }
       const int u = t - G;
       if (u >= 0 && u <= 2 * n_tiles) {
@@ -658,26 +649,26 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
         }
       }
       if constexpr ((TM & 1) == 1) wait_vmem();
-      if (t < 2 * n_tiles + 1) phase_barrier8();
+      if (t < 2 * n_tiles + 1) phase_barrier();
     };
     for (int t = 0; t < 2 * n_tiles + 2; t += 4) {
-      phase(t, ic8<0>{});
-      phase(t + 1, ic8<1>{});
+      phase(t, ic<0>{});
+      phase(t + 1, ic<1>{});
       if (t + 2 < 2 * n_tiles + 2) {
-        phase(t + 2, ic8<2>{});
-        phase(t + 3, ic8<3>{});
+        phase(t + 2, ic<2>{});
+        phase(t + 3, ic<3>{});
       }
     }
   };
 
-  if (group == 0) copy_pair(0, ic8<0>{});
+  if (group == 0) copy_pair(0, ic<0>{});
 #pragma unroll
   for (int c = 0; c < V_BYTES / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
   wait_vmem();
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zero-fill has landed
-  phase_barrier8();
-  if (group == 0) run(ic8<0>{});
-  else run(ic8<1>{});
+  phase_barrier();
+  if (group == 0) run(ic<0>{});
+  else run(ic<1>{});
   l_run = fmaf(lacc[0], inv_gain_prev, l_run);   // the last tile
 
   const float l_tot = l_run;

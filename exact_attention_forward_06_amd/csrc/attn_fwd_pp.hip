@@ -1,9 +1,15 @@
 // Exact-attention forward for gfx950, fp16 / bf16 inputs, d = 64 and 128:
-// the "ping-pong" schedule.  Computes the same result as attn_fwd.hip (the
-// FlashAttention-2 forward of the "FlashAttention-2/3" page: outer loop over
-// Q blocks, online softmax, one division by l at the end, LSE = m + ln l),
-// with a different division of the work inside a compute unit.
+// fp32 accumulation, causal or non-causal, per-row logsumexp output.
 //
+// Method (sources on the pages are listed in include/attn.h): the grid runs
+// over (batch, head, block of 256 query rows) -- the "outer loop over Q
+// blocks" of the FlashAttention-2 work partition ("FlashAttention-2/3" page,
+// FlashAttention-2 改进二) -- and each workgroup streams the K/V blocks of its
+// head through LDS, keeping the running row max m, the running row sum l and
+// the unnormalised output in registers; O is divided by l once after the
+// last block (改进一) and LSE = m + ln l is stored.
+//
+// Work inside a compute unit: the "ping-pong" schedule.
 //  * One workgroup of 8 wave64 per CU covers 256 query rows (32 per wave), so
 //    every K/V tile copied into LDS serves 8 waves.
 //  * Waves w and w + 4 run on the same SIMD.  Waves 0-3 (group 0) and 4-7
@@ -25,15 +31,44 @@
 //    runs both products, so S and O stay in fixed registers: control flow
 //    that merged different phase variants made the compiler copy all of O
 //    at every phase.
-//  * K_j and V_{j-1} are copied global -> LDS (buffer_load ... lds) two
+//  * K_j and V_{j-1} are copied global -> LDS (buffer_load ... lds, no VGPR
+//    staging; rows past N read as zero through the buffer range check) two
 //    phases before they are read, into one of two LDS stages; each stage is
 //    its own LDS object and the phase loop is unrolled so that every access
 //    names its stage at compile time.  Only group 1 issues the copies, at
 //    the start of its softmax phases: an LDS-DMA instruction holds the
 //    issuing wave while the CU's address unit takes its 1 KiB, which would
 //    stall the MFMA phase of the other group.
-// Operand layouts, the key permutation, the LDS swizzle, the lazy rescale
-// and the causal skipping are those of attn_fwd.hip.
+//
+// Operand mapping (shared with attn_fwd_pair.hip and attn_bwd.hip)
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} with Q^T resident in
+//    VGPRs.  A lane's accumulator holds ONE query (lane & 31) and 16 of a
+//    32-key block (the other 16 in lane ^ 32): row max / row sum are in-lane
+//    plus one v_permlane32_swap -- no LDS, each wave owns its rows (the
+//    page's "split Q across warps" partition, 改进三).
+//  * K rows are fed to that MFMA in a permuted order (bits 2 and 3 of the
+//    A-operand row swapped) so accumulator registers 8c..8c+7 hold 8
+//    consecutive keys; rounded to 16 bits they are directly the P^T operand
+//    of O^T += V^T P^T.  P never leaves VGPRs.
+//  * V stays in its natural [key][d] layout in LDS; the V^T operand is read
+//    with ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-d block
+//    and receives it transposed: one d per lane, 4 consecutive keys).
+//  * LDS rows are unpadded (the LDS-DMA writes 1 KiB per instruction
+//    contiguously), so 16-byte chunks are XOR-swizzled within a row; the
+//    swizzle makes both the K operand reads (16 rows, one chunk) and the
+//    transposed V reads (4 rows x 4 chunks) hit distinct banks.
+//  * Online softmax in the log2 domain with a lazy rescale: the running max
+//    is a whole number and only moves when a row's tile max exceeds it by
+//    more than 8, so P <= 256 and the O rescale -- an exact power of two --
+//    is skipped on almost every tile.  Row sums are accumulated from the
+//    fp32 P (the LSE keeps fp32 accuracy).
+//  * Causal: K/V tiles wholly above the workgroup's diagonal are never
+//    loaded; a wave whose rows all precede a tile skips its math; the element
+//    mask runs only where a tile straddles the diagonal or the end of the
+//    sequence.
+//  * Workgroup ids are remapped so that the Q blocks of a head run on one
+//    XCD (the head's K/V is then re-read from that XCD's L2); under the
+//    causal mask the Q blocks with the most K/V tiles are issued first.
 #include "attn16_common.h"
 #include "kernels.h"
 
@@ -43,25 +78,6 @@
 
 namespace attn {
 namespace {
-
-template <int V>
-using ic = std::integral_constant<int, V>;
-
-// Workgroup barrier between phases.  s_barrier alone is not a memory
-// operation to the compiler, which could then move LDS reads of a stage
-// across it (ahead of the barrier that publishes the stage's copy); the
-// empty asm statements with a memory clobber pin every memory access to its
-// side of the barrier.  No wait is implied: copies are waited for with
-// wait_vmem() and each phase consumes its own LDS reads.
-__device__ __forceinline__ void phase_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt lgkmcnt(0): this wave's LDS writes have completed
-// (simm16 = vmcnt 63 | expcnt 7 << 4 | lgkmcnt 0 << 8).
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // SPLIT: the grid also runs over p.nsplit key ranges; each workgroup covers
 // one range and writes that range's normalised O (fp32) and LSE to o_part
@@ -150,7 +166,7 @@ void attn_fwd_pp_kernel(Params p) {
     dma_off[t] = row * rbg + chunk * 16;
   }
 
-  // LDS read addresses (as in attn_fwd.hip): K A-operand row kb*32 +
+  // LDS read addresses: K A-operand row kb*32 +
   // key_of_row(n), logical chunk 2 ks + g; V^T A-operand via tr16 reads.
   const int krow = key_of_row(n);
   const int kswz = swz<D>(krow);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -16,6 +18,23 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Workgroup barrier between the phases of the ping-pong kernels.  s_barrier
+// alone is not a memory operation to the compiler, which could then move LDS
+// accesses across it; the empty asm statements with a memory clobber pin
+// every memory access to its side of the barrier.  No wait is implied.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses have completed
+// (simm16 = vmcnt 63 | expcnt 7 << 4 | lgkmcnt 0 << 8).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Cross-half reductions: lanes l and l ^ 32 hold the two halves of a row.
 // v_permlane32_swap returns both register images; one of them carries the

@@ -92,8 +92,9 @@ struct BwdArgs {
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_hadamard_rotate_quant(const QuantArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* supported);
-// split-KV partials (bf16 / fp16, d = 64 and 128) and their merge
+// split-KV partials (bf16 / fp16; d = 64 and 128, and d = 256) and their merge
 hipError_t launch_attn_fwd16_pp_split(const FwdArgs& a, hipStream_t stream, bool* supported);
+hipError_t launch_attn_fwd16_pair_split(const FwdArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream, bool* supported);
 // backward: dq kernel (also writes delta) then dk/dv kernel (fp16 / bf16, d = 64 and 128)
 hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream, bool* supported);

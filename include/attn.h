@@ -130,7 +130,7 @@ static inline int attn_splitkv_chunk(int N, int S) {
  * attn_fwd_splitkv -- attn_fwd computed as S key-range partials plus a merge.
  *
  *   dtype          ATTN_F16 or ATTN_BF16 (others: ATTN_ERR_UNSUPPORTED).
- *   B, H, N, d     as in attn_fwd; d in {64, 128} (256: ATTN_ERR_UNSUPPORTED).
+ *   B, H, N, d     as in attn_fwd; d in {64, 128, 256}.
  *   q, k, v, qkv_strides, softmax_scale, causal, stream   as in attn_fwd.
  *   num_splits     S, 1 <= S <= ATTN_MAX_SPLITS.
  *   o_part         device fp32 [S, B, H, N, d] workspace, written with each

@@ -156,7 +156,6 @@ def _split(lib, dtype=2, B=1, H=1, N=256, d=128, q=A, k=B_, v=C, strides=None, S
     (dict(S=0), 1, "num_splits"),
     (dict(S=65), 1, "num_splits"),
     (dict(dtype=0), 2, "fp16 / bf16"),
-    (dict(d=256), 2, "fp16 / bf16"),
     (dict(d=40), 2, "head dimension"),
     (dict(op=A), 1, "overlaps an input"),
     (dict(lp=O), 1, "overlap each other"),

@@ -137,11 +137,37 @@ def test_small_shapes(dtype, d, causal, N):
     _full_compare(inp, causal, dtype, f"{dtype} d={d} N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_multi_tile_ragged(causal):
+def test_multi_tile_ragged(causal, d):
     # several Q blocks and K/V tiles, ragged tail, B*H > 1
-    inp = make_inputs(2, 3, 1000, 128, "bf16", seed=7)
-    _full_compare(inp, causal, torch.bfloat16, f"N=1000 causal={causal}")
+    inp = make_inputs(2, 3, 1000, d, "bf16", seed=7 if d == 128 else 8)
+    _full_compare(inp, causal, torch.bfloat16, f"N=1000 d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_split_tile_row_max(causal):
+    """At d = 256 two waves share each 32-row query block, each taking half
+    of the keys of every 64-key tile for S and half of d for O, and they
+    agree on the row max of each tile through LDS.  Here every tile holds
+    one dominant key, alternately in its first and its second 32 keys: in
+    head 0 the peaks rise by about 10 (log2 units) per tile, so the running
+    max moves -- and O is rescaled -- at every tile, from either half; in
+    head 1 they fall, so the max stays with the first tile.  N = 340 leaves
+    the second half of the last tile wholly past N."""
+    B, H, N, d = 1, 2, 340, 256
+    base = make_inputs(B, H, N, d, "bf16", seed=31)
+    q, k = base["q"].float(), base["k"].float()
+    q[..., 0] = 4.0
+    k[..., 0] = 0.0
+    n_t = (N + 63) // 64
+    for t in range(n_t):
+        pos = 64 * t + (40 if t % 2 else 10)
+        pos = pos if pos < N else 64 * t + 5
+        k[0, 0, pos, 0] = 28.0 * t
+        k[0, 1, pos, 0] = 28.0 * (n_t - 1 - t)
+    inp = dict(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), v=base["v"])
+    _full_compare(inp, causal, torch.bfloat16, f"split-tile row max causal={causal}")
 
 
 def test_strided_bnhd_layout():
@@ -167,8 +193,9 @@ def test_custom_scale_and_no_lse():
     assert torch.equal(o1, o2)
 
 
-def test_bitwise_deterministic():
-    inp = make_inputs(2, 4, 1500, 128, "bf16", seed=11)
+@pytest.mark.parametrize("d", [128, 256])
+def test_bitwise_deterministic(d):
+    inp = make_inputs(2, 4, 1500, d, "bf16", seed=11)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     o1, l1 = attn_fwd(q, k, v, causal=True)
     o2, l2 = attn_fwd(q, k, v, causal=True)

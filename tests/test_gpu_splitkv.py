@@ -35,7 +35,7 @@ def _check(o_gpu, lse_gpu, o_ref, lse_ref, what):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,S", [(300, 3), (512, 1), (1000, 7), (130, 2), (200, 64)])
 def test_splitkv_matches_oracle(dtype, d, causal, N, S):
@@ -110,7 +110,7 @@ def test_merge_matches_oracle(d, out):
         np.testing.assert_allclose(og, o_ref, rtol=2 ** -8, atol=1e-3)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_two_tilings_agree(dtype, d, causal):
