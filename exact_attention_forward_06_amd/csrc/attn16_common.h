@@ -20,6 +20,8 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
+// 2^kTau: a lane's sum of P over a tile above this may hide a P above 2^kTau
+constexpr float kRescaleSum = 256.f;
 
 // s_waitcnt vmcnt(0): this wave's global -> LDS copies have landed
 // (simm16 = vmcnt 0 | expcnt 7 << 4 | lgkmcnt 15 << 8).

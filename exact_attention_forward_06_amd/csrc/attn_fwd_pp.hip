@@ -219,7 +219,7 @@ void attn_fwd_pp_kernel(Params p) {
   f32x16_t sacc[NKB];
   frag pf[NCC];
 
-  auto tile_max = [&](int kt0) __attribute__((always_inline)) -> float {   // kt0: global key index
+  auto mask_tile = [&](int kt0) __attribute__((always_inline)) {   // kt0: global key index
     const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
@@ -230,6 +230,8 @@ void attn_fwd_pp_kernel(Params p) {
           if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
         }
     }
+  };
+  auto tile_max = [&]() __attribute__((always_inline)) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -252,7 +254,8 @@ void attn_fwd_pp_kernel(Params p) {
       m_run = m_new;
     }
   };
-  auto softmax_p = [&]() __attribute__((always_inline)) {
+  // P_j = exp2(S_j c - m_run) into pf; returns this lane's sum of P
+  auto softmax_p = [&]() __attribute__((always_inline)) -> float {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -269,7 +272,31 @@ void attn_fwd_pp_kernel(Params p) {
       }
       pf[cc] = __builtin_bit_cast(frag, w);
     }
-    l_run += rs0 + rs1;
+    return rs0 + rs1;
+  };
+  // Softmax phase of the tile at global key kt0.  P is first taken against
+  // the running max as it stands.  A lane's sum of P bounds each of its P,
+  // so while no lane's sum exceeds 2^kTau no score of the tile is more than
+  // kTau above the running max and the lazy rescale would leave it where it
+  // is: the tile's max is then never needed.  Otherwise (and on a wave's
+  // first tile, where the running max is still -inf) the exact step runs:
+  // tile max, rescale rule, P again.  The running max thus follows the same
+  // sequence as with the max taken on every tile.  (One call site each for
+  // update_max and for the second softmax_p: the compiler copies all of O
+  // where control flow merges differently rescaled versions of it.)
+  auto softmax_tile = [&](int kt0) __attribute__((always_inline)) {
+    mask_tile(kt0);
+    float rs = 0.f;
+    bool exact = __any(m_run == -INFINITY);
+    if (!exact) {
+      rs = softmax_p();
+      exact = __any(rs > kRescaleSum);
+    }
+    if (exact) {
+      update_max(tile_max());
+      rs = softmax_p();
+    }
+    l_run += rs;
   };
 
   // MFMA phase: S^T of tile j from K stage `kst` (DQ) and O^T += V^T P^T of
@@ -349,8 +376,7 @@ void attn_fwd_pp_kernel(Params p) {
           // stage 0 is zero-filled, so O^T gains exactly zero.
           if (j <= w_tiles) phase_mfma(ic<1>{}, ic<1>{}, kst, vst);
         } else if (j < w_tiles) {
-          update_max(tile_max((j_base + j) * BN));
-          softmax_p();
+          softmax_tile((j_base + j) * BN);
         }
       }
       if constexpr ((TM & 1) == 1) wait_vmem();

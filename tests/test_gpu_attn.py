@@ -145,6 +145,32 @@ def test_multi_tile_ragged(causal, d):
     _full_compare(inp, causal, torch.bfloat16, f"N=1000 d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tile_sum_above_threshold(causal, d):
+    """The forward takes P against the running max as it stands and takes a
+    tile's exact max only when some lane's sum of P exceeds 2^8.  Scores
+    here (log2 units, all queries alike): key 0 at 0 and the rest of keys
+    0-127 at -10, so the running max starts at 0; keys 128-255 all at about
+    7, so every lane's sum is far above 2^8 while no score is more than 8
+    above the running max (the exact step runs and leaves the max alone);
+    one key of 256-383 at about 9.5 (the exact step moves the max); random
+    scores after that."""
+    B, H, N = 1, 2, 700
+    base = make_inputs(B, H, N, d, "bf16", seed=41 + d)
+    q, k = base["q"].float(), base["k"].float()
+    unit = 4.0 * (1 / math.sqrt(d)) * 1.4426950408889634   # score in log2 units per unit of k[..., 0]
+    q[..., 0] = 4.0
+    q[..., 1:] = 0.0
+    k[..., 0] = -10.0 / unit
+    k[:, :, 0, 0] = 0.0
+    k[:, :, 128:256, 0] = 7.0 / unit
+    k[:, :, 300, 0] = 9.5 / unit
+    k[:, :, 384:, 0] = torch.randn(B, H, N - 384, generator=torch.Generator().manual_seed(3)) * 2.0 / unit
+    inp = dict(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), v=base["v"])
+    _full_compare(inp, causal, torch.bfloat16, f"tile sum above 2^8 d={d} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_d256_split_tile_row_max(causal):
     """At d = 256 two waves share each 32-row query block, each taking half
