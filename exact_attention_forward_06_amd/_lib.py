@@ -35,6 +35,8 @@ _SIGNATURES = {
     "hadamard_rotate_quant_per_tensor": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "attn_fwd_fp8": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, ctypes.c_float,
                       _i, _vp], _i),
+    "attn_fwd_fp8_qrot": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                           ctypes.c_float, _i, _vp], _i),
     "attn_fwd_splitkv": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                           ctypes.c_float, _i, _vp], _i),
     "attn_merge": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
@@ -256,6 +258,37 @@ def attn_fwd_fp8(q8, q_scale, k8, k_scale, v8t, v_scale, causal=False, softmax_s
     _check(lib.attn_fwd_fp8(B, H, N, d, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
                             _ptr(v8t), _ptr(v_scale), block_rows, FP8_FORMATS[fp8_format], _ptr(out),
                             _ptr(lse), scale, int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def attn_fwd_fp8_qrot(q, signs, k8, k_scale, v8t, v_scale, causal=False, softmax_scale=None,
+                      block_rows=128, out=None, lse=None, return_lse=True, stream=None, fp8_format="e4m3"):
+    """attn_fwd_fp8 with Q rotated (signs, the int8 [d] diagonal K was rotated
+    with) and quantised by the attention kernel itself: q is fp16 / bf16
+    [B,H,N,d] with a contiguous last dim; k8, k_scale, v8t, v_scale as in
+    attn_fwd_fp8.  Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    lib = load()
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be fp16 or bf16")
+    B, H, N, d = q.shape
+    strides = _bhnd_strides(q)
+    for t in (k8, v8t, k_scale, v_scale, signs):
+        if not t.is_contiguous():
+            raise ValueError("attn_fwd_fp8_qrot takes contiguous codes, scales and signs")
+    nblk = -(-N // block_rows)
+    for name, t, shape, dt in (("k8", k8, (B, H, N, d), torch.uint8), ("v8t", v8t, (B, H, d, N), torch.uint8),
+                               ("k_scale", k_scale, (B, H, nblk), torch.float32),
+                               ("v_scale", v_scale, (B, H, nblk), torch.float32),
+                               ("signs", signs, (d,), torch.int8)):
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"{name} must be {dt} of shape {shape}; got {t.dtype} {tuple(t.shape)}")
+    out = _buf(out, (B, H, N, d), torch.bfloat16, q.device, "out")
+    if lse is not None or return_lse:
+        lse = _buf(lse, (B, H, N), torch.float32, q.device, "lse")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_fp8_qrot(_DTYPE_CODE[q.dtype], B, H, N, d, _ptr(q), strides, _ptr(signs), _ptr(k8),
+                                 _ptr(k_scale), _ptr(v8t), _ptr(v_scale), block_rows, FP8_FORMATS[fp8_format],
+                                 _ptr(out), _ptr(lse), scale, int(bool(causal)), _stream(stream)))
     return out, lse
 
 

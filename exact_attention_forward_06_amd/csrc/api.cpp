@@ -478,6 +478,74 @@ int attn_fwd_fp8(int B, int H, int N, int d, const uint8_t* q8, const float* q_s
   return hip_status(e, "attn_fwd_fp8 launch");
 }
 
+int attn_fwd_fp8_qrot(int dtype, int B, int H, int N, int d, const void* q, const int64_t* q_strides,
+                      const int8_t* signs, const uint8_t* k8, const float* k_scale, const uint8_t* v8t,
+                      const float* v_scale, int block_rows, int fp8_format, void* o, float* lse,
+                      float softmax_scale, int causal, void* stream) {
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARGUMENT,
+                "attn_fwd_fp8_qrot takes fp16 or bf16 q (dtype %d)", dtype);
+  if (int st = check_sizes(B, H, N, d)) return st;
+  if (int st = check_scale_causal(softmax_scale, causal)) return st;
+  if (block_rows != 128) return fail(ATTN_ERR_INVALID_ARGUMENT, "block_rows must be 128");
+  if (fp8_format != ATTN_FP8_E4M3 && fp8_format != ATTN_FP8_E5M2)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown fp8_format %d", fp8_format);
+  if (d == 256) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8_qrot covers d = 64 and 128");
+  if (N % block_rows != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8_qrot needs N a multiple of block_rows");
+  if ((int64_t)N * d >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one head's codes span 2 GiB or more");
+  int64_t sb, sh, sn;
+  strides_or_contiguous(q_strides, H, N, d, &sb, &sh, &sn);
+  const int64_t codes = (int64_t)B * H * N * d;
+  const int64_t nsc = (int64_t)B * H * (N / block_rows) * 4;
+  Span sq, ssg, a2, a3, b2, b3, so, sl{0, 0};
+  if (int st = check_strided("q", q, B, H, N, d, sb, sh, sn, 2, &sq)) return st;
+  if (int st = check_dense("signs", signs, d, &ssg)) return st;
+  if (int st = check_dense("k8", k8, codes, &a2)) return st;
+  if (int st = check_dense("v8t", v8t, codes, &a3)) return st;
+  if (int st = check_dense("k_scale", k_scale, nsc, &b2, false)) return st;
+  if (int st = check_dense("v_scale", v_scale, nsc, &b3, false)) return st;
+  if (int st = check_dense("o", o, codes * 2, &so)) return st;
+  if (lse) {
+    if (int st = check_dense("lse", lse, (int64_t)B * H * N * 4, &sl, false)) return st;
+  }
+  const Span ins[6] = {sq, ssg, a2, a3, b2, b3};
+  for (const Span& s : ins) {
+    if (overlaps(so, s) || (lse && overlaps(sl, s)))
+      return fail(ATTN_ERR_INVALID_ARGUMENT, "an output overlaps an input");
+  }
+  if (lse && overlaps(sl, so)) return fail(ATTN_ERR_INVALID_ARGUMENT, "lse overlaps o");
+
+  attn::Fp8FwdArgs a;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.q8 = nullptr;
+  a.q_scale = nullptr;
+  a.k8 = k8;
+  a.k_scale = k_scale;
+  a.v8t = v8t;
+  a.v_scale = v_scale;
+  a.block_rows = block_rows;
+  a.fp8_format = fp8_format;
+  a.o = o;
+  a.lse = lse;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  a.qx = q;
+  a.q_dtype = static_cast<attn::Dtype>(dtype);
+  a.qsb = sb;
+  a.qsh = sh;
+  a.qsn = sn;
+  a.signs = signs;
+  bool supported = true;
+  hipError_t e = attn::launch_attn_fwd_fp8(a, static_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(ATTN_ERR_UNSUPPORTED, "no attn_fwd_fp8_qrot kernel for d=%d", d);
+  return hip_status(e, "attn_fwd_fp8_qrot launch");
+}
+
 }  // extern "C"
 
 namespace {

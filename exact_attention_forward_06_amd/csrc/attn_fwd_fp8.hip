@@ -70,7 +70,21 @@ struct F8Params {
   float* lse;
   int H, N, nmb, total, nblk;
   float scale_log2;
+  // Q rotated and quantised in the kernel (ping-pong kernel, QR != 0)
+  const char* qx;
+  const int8_t* signs;
+  int64_t qsb, qsh, qsn;
 };
+
+template <typename T>
+__device__ __forceinline__ float q_to_f32(T v) { return (float)v; }
+
+// Wave-wide maximum (all 64 lanes).
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
@@ -387,7 +401,9 @@ void attn_fwd_fp8_kernel(F8Params p) {
 // unit accepts it (about 256 cycles for a 32 KiB pair), which the MFMA phase
 // absorbs in its wait at the barrier.
 
-template <int D, bool CAUSAL, int FMT>
+// QR: 0 = Q8 codes and scales from the pre-pass; 1 (bf16) or 2 (fp16) =
+// 16-bit Q rotated and quantised in the prologue (see the prologue).
+template <int D, bool CAUSAL, int FMT, int QR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_pp_kernel(F8Params p) {
   constexpr int BN = 128, NT = 512, NTC = 256, BLOCK_M = 256;
@@ -433,9 +449,6 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   typedef __attribute__((address_space(4))) const float cfloat_t;
   cfloat_t* ksc = (cfloat_t*)(p.ks + (int64_t)bh * p.nblk);
   cfloat_t* vsc = (cfloat_t*)(p.vs + (int64_t)bh * p.nblk);
-  const float sq_raw = (wq0 < N) ? p.qs[(int64_t)bh * p.nblk + (wq0 >> 7)] : 1.f;
-  const float sq = sq_raw > 0.f ? sq_raw : 1.f;
-
   float svmax = 0.f;
   for (int i = 0; i < p.nblk; ++i) svmax = fmaxf(svmax, vsc[i]);
   if (!(svmax > 0.f)) svmax = 1.f;     // every V block is zero: O = 0
@@ -443,7 +456,9 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
 
   // Q8^T fragments: lane (n, g) holds Q8[q][64 ks + 32 g .. +32]
   i32x8_t qf[NKS];
-  {
+  float sq_raw = 1.f;
+  if constexpr (QR == 0) {
+    sq_raw = (wq0 < N) ? p.qs[(int64_t)bh * p.nblk + (wq0 >> 7)] : 1.f;
     const uint8_t* src = p.q8 + head + (int64_t)q_row * D + g * 32;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -455,6 +470,95 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
       qf[ks] = cat(lo, hi);
     }
   }
+  // (QR != 0) run after the first tile copy has been issued, so that the
+  // copy's latency overlaps this work
+  auto q_prologue = [&]() __attribute__((always_inline)) {
+    // The pre-pass's work on Q, done here on the rows the kernel needs anyway
+    // (the "Hadamard in the kernel" of the "FlashAttention-3" page, section
+    // "为什么 Hadamard 适合放到内核里"): x~ = H D x over d for each row, then
+    // per 128-row block (the four waves of a group) amax = max |x~|,
+    // code = E4M3(x~ * 448 / amax), scale = amax / (448 sqrt(d)) -- the same
+    // arithmetic as hadamard_quant.hip, in the lane layout of the B operand:
+    // element e of lane (n, g)'s fragment ks is d index 64 ks + 32 g + e.
+    // The transform is unnormalised; its butterfly stages run over the bits
+    // of e in the lane, over ks across fragments and over g across lanes
+    // n and n + 32.  (The stages commute, so the order of summation differs
+    // from the pre-pass and the rotated values may differ in the last bit.)
+    using QT = std::conditional_t<QR == 1, __bf16, _Float16>;
+    constexpr float QMAX = FMT == 0 ? 448.f : 57344.f;
+    const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+    const char* src = p.qx + ((int64_t)b_ * p.qsb + (int64_t)h_ * p.qsh + (int64_t)q_row * p.qsn) * 2 + g * 64;
+    float x[NKS][32];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        u32x4_t raw = {0u, 0u, 0u, 0u};
+        if (q_row < N) raw = *(const u32x4_t*)(src + ks * 128 + l * 16);
+        const QT* e = reinterpret_cast<const QT*>(&raw);
+        u32x2_t sraw = *(const u32x2_t*)(p.signs + ks * 64 + g * 32 + l * 8);
+        const int8_t* sg = reinterpret_cast<const int8_t*>(&sraw);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[ks][l * 8 + t] = q_to_f32<QT>(e[t]) * (float)sg[t];
+      }
+#pragma unroll
+    for (int hh = 1; hh < 32; hh <<= 1)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if ((e & hh) == 0) {
+            const float a = x[ks][e], c = x[ks][e + hh];
+            x[ks][e] = a + c;
+            x[ks][e + hh] = a - c;
+          }
+    if constexpr (NKS == 2) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float a = x[0][e], c = x[1][e];
+        x[0][e] = a + c;
+        x[1][e] = a - c;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float o = __shfl_xor(x[ks][e], 32);
+        x[ks][e] = g ? o - x[ks][e] : x[ks][e] + o;
+        amax = fmaxf(amax, fabsf(x[ks][e]));
+      }
+    __shared__ float qred[8];
+    amax = wave_max64(amax);
+    if (lane == 0) qred[wave] = amax;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    phase_barrier();
+    const int w0 = wave & 4;               // the group's four waves: one 128-row scale block
+    amax = fmaxf(fmaxf(qred[w0], qred[w0 + 1]), fmaxf(qred[w0 + 2], qred[w0 + 3]));
+    sq_raw = amax * (1.f / sqrtf((float)D)) / QMAX;   // 0 for a zero block
+    const float ramax = amax > 0.f ? 1.f / amax : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float a = x[ks][4 * w + t] * QMAX;
+          const float y0 = a * ramax;
+          const float q = fmaf(fmaf(-y0, amax, a), ramax, y0);
+          y[t] = fminf(fmaxf(q, -QMAX), QMAX);
+        }
+        if constexpr (FMT == 0) {
+          const unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          qf[ks][w] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+        } else {
+          const unsigned lo = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+          qf[ks][w] = (int)__builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], lo, true);
+        }
+      }
+  };
 
   // copies by the 256 threads of group 0
   const __amdgpu_buffer_rsrc_t krs =
@@ -500,7 +604,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   const int kv_end = CAUSAL ? min(N, m0 + BLOCK_M) : N;
   const int n_tiles = kv_end / BN;     // N is a multiple of 128
   const int w_tiles = (wq0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (wq0 + 31) / BN + 1) : n_tiles);
-  const float c0 = sq * p.scale_log2;
+  float c0 = 0.f;   // sq * scale * log2(e), set once Q's scale is known
 
   f32x16_t sacc[NKB];
   i32x8_t pf[NPV];
@@ -664,6 +768,8 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   if (group == 0) copy_pair(0, ic<0>{});
 #pragma unroll
   for (int c = 0; c < V_BYTES / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
+  if constexpr (QR != 0) q_prologue();
+  c0 = (sq_raw > 0.f ? sq_raw : 1.f) * p.scale_log2;
   wait_vmem();
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zero-fill has landed
   phase_barrier();
@@ -692,7 +798,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   }
 }
 
-template <int D, bool CAUSAL, int FMT>
+template <int D, bool CAUSAL, int FMT, int QR>
 hipError_t launch_pp(const Fp8FwdArgs& a, hipStream_t s) {
   constexpr int BLOCK_M = 256;
   F8Params p;
@@ -710,7 +816,12 @@ hipError_t launch_pp(const Fp8FwdArgs& a, hipStream_t s) {
   p.total = a.B * a.H * p.nmb;
   p.nblk = a.N / a.block_rows;
   p.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_fp8_pp_kernel<D, CAUSAL, FMT>), dim3(p.total), dim3(512), 0, s, p);
+  p.qx = static_cast<const char*>(a.qx);
+  p.signs = a.signs;
+  p.qsb = a.qsb;
+  p.qsh = a.qsh;
+  p.qsn = a.qsn;
+  hipLaunchKernelGGL((attn_fwd_fp8_pp_kernel<D, CAUSAL, FMT, QR>), dim3(p.total), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -743,9 +854,24 @@ hipError_t launch_mask(const Fp8FwdArgs& a, hipStream_t s) {
 
 template <int FMT>
 hipError_t launch_fmt(const Fp8FwdArgs& a, hipStream_t stream, bool* supported) {
+  if (a.qx) {   // Q rotated and quantised in the ping-pong kernel's prologue
+    auto go = [&](auto qr) -> hipError_t {
+      constexpr int QR = decltype(qr)::value;
+      switch (a.d) {
+        case 64: return a.causal ? launch_pp<64, true, FMT, QR>(a, stream) : launch_pp<64, false, FMT, QR>(a, stream);
+        case 128: return a.causal ? launch_pp<128, true, FMT, QR>(a, stream) : launch_pp<128, false, FMT, QR>(a, stream);
+      }
+      *supported = false;
+      return hipSuccess;
+    };
+    if (a.q_dtype == Dtype::BF16) return go(ic<1>{});
+    if (a.q_dtype == Dtype::F16) return go(ic<2>{});
+    *supported = false;
+    return hipSuccess;
+  }
   switch (a.d) {
-    case 64: return a.causal ? launch_pp<64, true, FMT>(a, stream) : launch_pp<64, false, FMT>(a, stream);
-    case 128: return a.causal ? launch_pp<128, true, FMT>(a, stream) : launch_pp<128, false, FMT>(a, stream);
+    case 64: return a.causal ? launch_pp<64, true, FMT, 0>(a, stream) : launch_pp<64, false, FMT, 0>(a, stream);
+    case 128: return a.causal ? launch_pp<128, true, FMT, 0>(a, stream) : launch_pp<128, false, FMT, 0>(a, stream);
     case 256: return launch_mask<256, 64, FMT>(a, stream);
   }
   *supported = false;

@@ -67,6 +67,12 @@ struct Fp8FwdArgs {
   float* lse;
   float scale;
   bool causal;
+  // Q rotated and quantised by the kernel (q8 and q_scale unused): 16-bit Q
+  // of dtype q_dtype at element strides (qsb, qsh, qsn), D = signs
+  const void* qx = nullptr;
+  Dtype q_dtype = Dtype::BF16;
+  int64_t qsb = 0, qsh = 0, qsn = 0;
+  const int8_t* signs = nullptr;
 };
 
 struct BwdArgs {

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 /* Status codes returned by every entry point. */
 enum {
@@ -263,6 +263,35 @@ int attn_fwd_fp8(int B, int H, int N, int d,
                  int block_rows, int fp8_format,
                  void* o, float* lse,
                  float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_fwd_fp8_qrot -- attn_fwd_fp8 with Q's incoherent processing and
+ * quantisation done by the attention kernel itself, on the rows it reads:
+ * the "FlashAttention-3" page, section "为什么 Hadamard 适合放到内核里" (the
+ * Hadamard transform placed in the kernel), with the per-block scales of the
+ * "FlashAttention-2/3" page, FlashAttention-3 特性三.  The result is that of
+ * hadamard_rotate_quant on q (with these signs) followed by attn_fwd_fp8:
+ * each 128-row block of Q gets amax, codes and scale by the same rule.  The
+ * fp32 sums of the transform run in another order than in the pre-pass, so
+ * a code may differ where the rotated value lies within a few fp32 ulps of a
+ * rounding midpoint.
+ *
+ *   dtype          ATTN_F16 or ATTN_BF16: the type of q.
+ *   q              device [B, H, N, d] at element strides q_strides (b, h, n;
+ *                  NULL = contiguous), d stride 1, 16-byte aligned rows.
+ *   signs          device int8 [d], the +-1 diagonal D (the one K's codes
+ *                  were rotated with), 16-byte aligned.
+ *   k8, k_scale, v8t, v_scale, block_rows, fp8_format, o, lse,
+ *   softmax_scale, causal, stream   as in attn_fwd_fp8.
+ *   d              64 or 128 (256: ATTN_ERR_UNSUPPORTED).
+ */
+int attn_fwd_fp8_qrot(int dtype, int B, int H, int N, int d,
+                      const void* q, const int64_t* q_strides, const int8_t* signs,
+                      const uint8_t* k8, const float* k_scale,
+                      const uint8_t* v8t, const float* v_scale,
+                      int block_rows, int fp8_format,
+                      void* o, float* lse,
+                      float softmax_scale, int causal, void* stream);
 
 /* Pairings of rope_hadamard_rotate_quant. */
 enum { ATTN_ROPE_INTERLEAVED = 1, ATTN_ROPE_HALF = 2 };

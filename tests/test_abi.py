@@ -36,10 +36,10 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"attn_abi_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "hadamard_rotate_quant", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_merge",
                           "attn_bwd", "rope_hadamard_rotate_quant", "attn_clock_probe", "attn_bwd_noalloc",
-                          "hadamard_rotate_quant_per_tensor"}
+                          "hadamard_rotate_quant_per_tensor", "attn_fwd_fp8_qrot"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
 
 
 @pytest.mark.parametrize("spin,out,msg", [(0, A, "spin_us"), (100001, A, "spin_us"), (10, None, "out is NULL"),
@@ -137,6 +137,37 @@ def _fp8(lib, B=1, H=1, N=256, d=128, q8=A, qs=A + 0x8000000, k8=B_, ks=B_ + 0x8
 ])
 def test_fp8_rejects(lib, kw, status, msg):
     assert _fp8(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+SG = 0x50000000      # signs
+
+
+def _fp8q(lib, dtype=2, B=1, H=1, N=256, d=128, q=A, strides=None, signs=SG, k8=B_, ks=B_ + 0x8000000, v8=C,
+          vs=C + 0x8000000, block_rows=128, fmt=0, o=O, lse=L, scale=0.088, causal=0):
+    s = None if strides is None else (ctypes.c_int64 * 3)(*strides)
+    return lib.attn_fwd_fp8_qrot(dtype, B, H, N, d, q, s, signs, k8, ks, v8, vs, block_rows, fmt, o, lse, scale,
+                                 causal, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(signs=None), 1, "signs is NULL"),
+    (dict(signs=SG + 4), 1, "signs is not 16-byte aligned"),
+    (dict(dtype=0), 2, "fp16 or bf16"),
+    (dict(dtype=9), 1, "fp16 or bf16"),
+    (dict(d=256), 2, "d = 64 and 128"),
+    (dict(d=48), 2, "head dimension"),
+    (dict(N=200), 2, "multiple of block_rows"),
+    (dict(block_rows=64), 1, "block_rows"),
+    (dict(fmt=2), 1, "fp8_format"),
+    (dict(strides=(256 * 128, 256 * 128, 100)), 1, "n stride < d"),
+    (dict(o=A), 1, "overlaps"),
+    (dict(lse=SG), 1, "overlaps"),
+    (dict(causal=2), 1, "causal"),
+])
+def test_fp8_qrot_rejects(lib, kw, status, msg):
+    assert _fp8q(lib, **kw) == status
     assert msg in lib.attn_last_error().decode()
 
 

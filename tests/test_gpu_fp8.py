@@ -36,7 +36,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_06_amd import attn_fwd_fp8, attn_fwd_fp8_e2e, hadamard_rotate_quant
+from exact_attention_forward_06_amd import attn_fwd_fp8, attn_fwd_fp8_e2e, attn_fwd_fp8_qrot, hadamard_rotate_quant
 from exact_attention_forward_06_amd.inputs import WORKLOADS, make_inputs, random_signs, to_f64, workload_inputs
 
 from oracle_pool import fp8_head_errors, map_heads, reduce_fp8
@@ -218,6 +218,69 @@ def test_fp8_attention_matches_simulation(d, causal, outliers, fmt):
     # the quantisation error itself stays in the range E4M3 allows
     exact, _ = oracle.attention(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), 1 / math.sqrt(d), causal)
     assert oracle.rel_rms(to_f64(o), exact) < 0.5
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("outliers", [False, True])
+@pytest.mark.parametrize("qdtype", ["bf16", "fp16"])
+def test_fp8_q_in_kernel_matches_simulation(d, causal, outliers, fmt, qdtype):
+    """attn_fwd_fp8_qrot: Q rotated and quantised by the attention kernel.
+    Against the oracle's simulation at the kernel gates, and against the
+    pre-pass path (hadamard_rotate_quant on Q, then attn_fwd_fp8), which it
+    must reproduce up to Q codes that flip at a rounding midpoint: relative
+    RMS between the two outputs <= 1e-3 (one flipped code moves a score by
+    at most one E4M3 step of one Q element)."""
+    B, H, N = 1, 2, 384
+    inp = _fp8_inputs(B, H, N, d, seed=d + 11, outliers=outliers)
+    if qdtype == "fp16":
+        inp = dict(inp, q=inp["q"].to(torch.float16))
+    q, k, v, sg = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["signs"].cuda()
+    o, lse = attn_fwd_fp8_e2e(q, k, v, sg, causal=causal, fp8_format=fmt, q_in_kernel=True)
+    o2, lse2 = attn_fwd_fp8_e2e(q, k, v, sg, causal=causal, fp8_format=fmt)
+    torch.cuda.synchronize()
+    sim_inp = dict(inp, q=inp["q"].to(torch.float32))
+    o_ref, lse_ref = _sim_p(sim_inp, causal, fmt=fmt)
+    _check_sim(o, lse, o_ref, lse_ref, f"q in kernel {qdtype} {fmt} d={d} causal={causal} outliers={outliers}")
+    between = oracle.rel_rms(to_f64(o), to_f64(o2))
+    print(f"  q in kernel vs pre-pass path: O rel RMS {between:.2e}", flush=True)
+    assert between <= 1e-3
+
+
+def test_fp8_q_in_kernel_workload(capsys):
+    """The FP8 workload (B=2 H=16 N=8192 d=128, outlier channel) through
+    attn_fwd_fp8_qrot, every head and row against the simulation at the
+    kernel gates."""
+    w = WORKLOADS["fp8_hadamard_8k"]
+    inp = workload_inputs(w)
+    q, k, v, sg = (inp[n].cuda() for n in ("q", "k", "v", "signs"))
+    o, lse = attn_fwd_fp8_e2e(q, k, v, sg, q_in_kernel=True)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    f32 = {n: inp[n].float().numpy() for n in ("q", "k", "v")}
+    tasks = [(f32["q"][b, h], f32["k"][b, h], f32["v"][b, h], inp["signs"].numpy(), o[b, h], lse[b, h], w.scale,
+              False) for b in range(w.B) for h in range(w.H)]
+    r = reduce_fp8(map_heads(fp8_head_errors, tasks))
+    with capsys.disabled():
+        print(f"\n[fp8 workload full, q in kernel] {r['heads']} heads: GPU vs simulation {r['gpu_vs_simp']:.2e}, "
+              f"|LSE err| mean {r['lse_simp_mean']:.2e} p99 {r['lse_simp_p99']:.2e}; vs exact "
+              f"{r['gpu_vs_exact']:.4f}", flush=True)
+    assert r["finite"] and r["heads"] == w.B * w.H
+    assert r["gpu_vs_simp"] <= O_TOL and r["lse_simp_p99"] <= LSE_TOL and r["lse_simp_mean"] <= LSE_MEAN_TOL, r
+
+
+def test_fp8_q_in_kernel_zero_q_block():
+    """An all-zero 128-row block of Q (scale 0, codes 0): its rows see
+    uniform weights, O is the mean of the visible V rows."""
+    B, H, N, d = 1, 1, 256, 128
+    inp = _fp8_inputs(B, H, N, d, seed=5, outliers=False)
+    inp["q"][0, 0, 128:] = 0
+    q, k, v, sg = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["signs"].cuda()
+    o, lse = attn_fwd_fp8_e2e(q, k, v, sg, q_in_kernel=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _sim_p(inp, False)
+    _check_sim(o, lse, o_ref, lse_ref, "q in kernel, zero Q block")
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
