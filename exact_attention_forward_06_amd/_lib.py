@@ -149,7 +149,7 @@ def splitkv_chunk(N: int, num_splits: int) -> int:
 def attn_fwd_splitkv(q, k, v, num_splits, causal=False, softmax_scale=None, out=None, lse=None,
                      o_part=None, lse_part=None, stream=None):
     """attn_fwd as num_splits key-range partials plus their merge (fp16 /
-    bf16, d = 64 or 128).  Returns (o, lse, o_part, lse_part); the partial
+    bf16, d = 64, 128 or 256).  Returns (o, lse, o_part, lse_part); the partial
     buffers (fp32 [S, B, H, N, d] and [S, B, H, N]) are allocated unless
     given."""
     lib = load()

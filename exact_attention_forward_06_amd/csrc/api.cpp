@@ -561,8 +561,7 @@ int bwd_prepare(int dtype, int B, int H, int N, int d, const void* q, const void
   if (es == 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (int st = check_sizes(B, H, N, d)) return st;
   if (int st = check_scale_causal(softmax_scale, causal)) return st;
-  if (dtype == ATTN_F32 || d == 256)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd covers fp16 / bf16 with d = 64 or 128");
+  if (dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd covers fp16 / bf16");
   const int64_t rows = (int64_t)B * H * N;
   const int64_t tbytes = rows * d * es;
   int64_t sb, sh, sn;

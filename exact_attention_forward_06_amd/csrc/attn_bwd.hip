@@ -1,4 +1,4 @@
-// Exact-attention backward for gfx950, fp16 / bf16 inputs with d = 64 or 128:
+// Exact-attention backward for gfx950, fp16 / bf16 inputs with d = 64, 128, 256:
 // dQ, dK, dV of O = softmax(Q K^T * scale) V for an upstream gradient dO,
 // with P recomputed tile by tile from the forward's stored logsumexp so that,
 // as in the forward, no N x N matrix reaches device memory.
@@ -14,7 +14,7 @@
 //     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K
 // (the chain rule through softmax; D_i = sum_j P_ij dP_ij = dO_i . O_i).
 //
-// Two launches, no atomics, deterministic:
+// Two launches (four at d = 256, below), no atomics, deterministic:
 //  * attn_bwd_dq_kernel: one workgroup per (b, h, 128 query rows); streams
 //    K/V tiles like the forward.  Its prologue also computes D_i from O and
 //    dO and stores it in the caller's workspace for the second launch.
@@ -39,6 +39,11 @@
 //  * dkdv kernel: the mirror image: S = Q K^T and dP = dO V^T with lane = one
 //    key; P and dS are the B operands of dV^T += dO^T P and dK^T += Q^T dS,
 //    with dO^T and Q^T read transposed from the streamed tiles.
+//  * d = 256: a wave cannot hold its 32 stationary rows of both operands
+//    (128 VGPRs) beside a full-width accumulator, so each gradient is built
+//    in two launches over its column halves (DH = 0, 1), each recomputing S
+//    and dP over the full d from 32-row streamed tiles; dK / dV use the
+//    4-wave dkdv kernel (K and V in VGPRs, dK and dV halves in AGPRs).
 //  * Causal: the dq kernel never loads K/V tiles past its block's last
 //    query; the dkdv kernel starts at the first Q tile that can see its
 //    block's keys.  Element masks run only on tiles that straddle the
@@ -75,25 +80,30 @@ constexpr int kBwdBlock = 128;     // stationary rows per workgroup (32 per wave
 constexpr int kBwdTile = 64;       // streamed rows per LDS tile
 
 // Row addresses inside an LDS tile of the swizzled [row][D] layout.
-//  rows(ks): the A operand "row-major" read -- lane (n, g) reads the 16 bytes
+//  row(ks): the A operand "row-major" read -- lane (n, g) reads the 16 bytes
 //    of logical chunk 2 ks + g of row key_of_row(n) (add kb * 32 * RB for the
 //    kb-th 32-row block).
 //  tr(db, half): the transposed read (ds_read_b64_tr_b16) -- lanes get one
 //    column d of 4 consecutive rows; add cc * 16 * RB for the cc-th 16-row
 //    chunk.
+//  The swizzle touches the low 4 bits of the chunk index only, so at d = 256
+//  the chunks 16..31 of a row sit 256 bytes after chunks 0..15: row(ks) of
+//  ks >= 8 is row(ks - 8) + 256, an immediate offset (8 registers saved).
 template <int D>
 struct TileAddr {
   static constexpr int RB = D * 2;
   static constexpr int NKS = D / 16;
+  static constexpr int NR = NKS < 8 ? NKS : 8;
   static constexpr int NDB = D / 32;
-  int rows[NKS];
+  int rows_[NR];
   int tr[NDB][2];
+  __device__ __forceinline__ int row(int ks) const { return rows_[ks % NR] + (ks / NR) * 256; }
   __device__ __forceinline__ explicit TileAddr(int lane) {
     const int n = lane & 31, g = lane >> 5;
     const int krow = key_of_row(n);
     const int kswz = swz<D>(krow);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) rows[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
+    for (int ks = 0; ks < NR; ++ks) rows_[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
     const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
     const int vg = hq >> 1;
     const int vcol0 = (hq & 1) * 16 + 4 * ta;
@@ -133,7 +143,7 @@ __device__ __forceinline__ void tile_dot(f32x16_t (&acc)[NKB], const char* tile,
     for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(tile + kb * 32 * TileAddr<D>::RB + ta.rows[ks]));
+      const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(tile + kb * 32 * TileAddr<D>::RB + ta.row(ks)));
       acc[kb] = Ops<T>::mfma(a, yf[ks], acc[kb]);
     }
   }
@@ -170,15 +180,20 @@ __device__ __forceinline__ void store_rowT(char* dst, const f32x16_t (&acc)[D / 
 // ---------------------------------------------------------------------------
 // dQ (and D_i).  Grid: (b, h, 128-query block), XCD-grouped per head; under
 // the causal mask the blocks with the most K/V tiles go first.
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// DH (d = 256 only): this launch accumulates dQ's columns 128 DH .. + 127;
+// S and dP always run over the full d, so the two halves' launches each
+// recompute them (a d = 256 wave cannot hold Q, dO and all of dQ at once).
+template <typename T, int D, bool CAUSAL, int DH = 0>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
 void attn_bwd_dq_kernel(BwdParams p) {
   using Op = Ops<T>;
   using frag = typename Op::frag;
-  constexpr int NT = kBwdThreads, BN = kBwdTile;
+  constexpr int NT = kBwdThreads, BN = D <= 128 ? kBwdTile : 32;
   constexpr int RB = D * 2;
   constexpr int TILE = BN * RB;
-  constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NCC = BN / 16;
+  constexpr int DO = D <= 128 ? D : 128;      // dQ columns of this launch
+  constexpr int D0 = DH * DO;                 // ... starting here
+  constexpr int NKS = D / 16, NKB = BN / 32, NDB = DO / 32, NCC = BN / 16;
   constexpr int LOADS = TILE / (NT * 16);
   static_assert(TILE % (NT * 16) == 0, "tile split");
 
@@ -225,7 +240,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < 8; ++e) part = fmaf((float)of[e], (float)dof[ks][e], part);
     }
     delta = pair_sum(part);
-    if (q_ok && g == 0) p.delta[head + q_row] = delta;
+    if (q_ok && g == 0 && DH == 0) p.delta[head + q_row] = delta;
   }
   const float lse2 = q_ok ? p.lse[head + q_row] * kLog2e : 0.f;
 
@@ -285,7 +300,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc)
-        dqacc[db] = Op::mfma(read_tr<frag, D>(kt + cc * 16 * RB, ta, db), dsf[cc], dqacc[db]);
+        dqacc[db] = Op::mfma(read_tr<frag, D>(kt + cc * 16 * RB, ta, db + D0 / 32), dsf[cc], dqacc[db]);
   };
 
   // The tile offset goes into the per-lane offset, which the buffer range
@@ -293,14 +308,22 @@ void attn_bwd_dq_kernel(BwdParams p) {
   // lane covers row t * RPT + lane_row of the tile; RPT is a multiple of 16,
   // so the swizzled chunk depends on the lane alone and the offsets differ by
   // a wave-uniform term (one live register: this kernel is at its limit).
+  // (At d = 256 an instruction covers 8 rows, half a swizzle period, so the
+  // offsets of even and odd instructions take their own swizzle.)
   constexpr int RPT = NT * 16 / RB;
-  static_assert(RPT % 16 == 0, "swizzle period");
+  constexpr int NOFF = RPT % 16 == 0 ? 1 : 16 / RPT;
+  static_assert(RPT % 16 == 0 || 16 % RPT == 0, "swizzle period");
   const int lane_row = tid * 16 / RB;
-  const int lane_off = lane_row * rbg + ((((tid * 16) % RB) / 16) ^ swz<D>(lane_row)) * 16;
+  int lane_off[NOFF];
+#pragma unroll
+  for (int u = 0; u < NOFF; ++u) {
+    const int row = u * RPT + lane_row;
+    lane_off[u] = lane_row * rbg + ((((tid * 16) % RB) / 16) ^ swz<D>(row)) * 16;
+  }
   auto copy = [&](int tile, int st) __attribute__((always_inline)) {
     int off[LOADS];
 #pragma unroll
-    for (int t = 0; t < LOADS; ++t) off[t] = lane_off + (tile * BN + t * RPT) * rbg;
+    for (int t = 0; t < LOADS; ++t) off[t] = lane_off[t % NOFF] + (tile * BN + t * RPT) * rbg;
     dma_tile<LOADS, NT>(krs, st ? sk1 : sk0, wave, 0, off);
     dma_tile<LOADS, NT>(vrs, st ? sv1 : sv0, wave, 0, off);
   };
@@ -322,21 +345,25 @@ void attn_bwd_dq_kernel(BwdParams p) {
     if (j + 1 < n_tiles) step(j + 1, 1);
   }
 
-  if (q_ok) store_rowT<T, D>(p.dq + row_off, dqacc, p.scale, g);
+  if (q_ok) store_rowT<T, DO>(p.dq + row_off + D0 * 2, dqacc, p.scale, g);
 }
 
 // ---------------------------------------------------------------------------
 // dK and dV.  Grid: (b, h, 128-key block), XCD-grouped per head; under the
 // causal mask the low key blocks (most Q tiles) come first in natural order.
-template <typename T, int D, bool CAUSAL>
+// DH (d = 256 only): this launch accumulates the columns 128 DH .. + 127 of
+// dK and dV; S and dP run over the full d in both halves' launches.
+template <typename T, int D, bool CAUSAL, int DH = 0>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1, D <= 64 ? 2 : 1)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
   using Op = Ops<T>;
   using frag = typename Op::frag;
-  constexpr int NT = kBwdThreads, BN = kBwdTile;
+  constexpr int NT = kBwdThreads, BN = D <= 128 ? kBwdTile : 32;
   constexpr int RB = D * 2;
   constexpr int TILE = BN * RB;
-  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int DO = D <= 128 ? D : 128;      // dK / dV columns of this launch
+  constexpr int D0 = DH * DO;                 // ... starting here
+  constexpr int NKS = D / 16, NDB = DO / 32;
   constexpr int LOADS = TILE / (NT * 16);
   static_assert(TILE % (NT * 16) == 0, "tile split");
 
@@ -344,9 +371,11 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sq1[TILE];
   __shared__ __attribute__((aligned(1024))) char so0[TILE];
   __shared__ __attribute__((aligned(1024))) char so1[TILE];
-  // per Q tile: LSE (64 floats) then D (64 floats)
-  __shared__ __attribute__((aligned(16))) float st0[2 * BN];
-  __shared__ __attribute__((aligned(16))) float st1[2 * BN];
+  // per Q tile: LSE at [0, 64) then D at [64, 128), one float per lane of
+  // the loading wave (at BN = 32 the upper 32 of each are the next tile's)
+  constexpr int SD = 64;
+  __shared__ __attribute__((aligned(16))) float st0[2 * SD];
+  __shared__ __attribute__((aligned(16))) float st1[2 * SD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -411,22 +440,6 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     const char* orows = ot + qb * 32 * RB;
     tile_dot<T, D, 1>(sacc, qrows, ta, kf);    // S = Q K^T   (lane = key)
     tile_dot<T, D, 1>(pacc, orows, ta, vf);    // dP = dO V^T
-    // LSE and D of the 16 queries of this lane's registers: register i holds
-    // query q0 + 16 (i >> 3) + 8 g + (i & 7)
-    float ls[16], dl[16];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int v4 = 0; v4 < 2; ++v4) {
-        const int idx = qb * 32 + 16 * h2 + 8 * g + 4 * v4;
-        const f32x4_t a = *(const f32x4_t*)(sts + idx);
-        const f32x4_t b = *(const f32x4_t*)(sts + BN + idx);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ls[8 * h2 + 4 * v4 + e] = a[e] * kLog2e;
-          dl[8 * h2 + 4 * v4 + e] = b[e];
-        }
-      }
     // masked scores -> -inf (P = 0, dS = 0), only on blocks that straddle
     // the diagonal or the end of the sequence
     if ((q0 + 32 > N) || (CAUSAL && q0 < wk0 + 31)) {
@@ -436,19 +449,26 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         if ((qi >= N) || (CAUSAL && key > qi)) sacc[0][i] = -INFINITY;
       }
     }
+    // register i holds query q0 + 16 (i >> 3) + 8 g + (i & 7); the LSE and D
+    // of a chunk's 8 queries are read from LDS as the chunk needs them
     frag pf[2], dsf[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
+      const float* sl = sts + qb * 32 + 16 * cc + 8 * g;
+      const f32x4_t l0 = *(const f32x4_t*)(sl), l1 = *(const f32x4_t*)(sl + 4);
+      const f32x4_t d0 = *(const f32x4_t*)(sl + SD), d1 = *(const f32x4_t*)(sl + SD + 4);
       u32x4_t wp, wd;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float pr2[2], ds2[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int i = cc * 8 + 2 * t + u;
-          const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], c, -ls[i]));
+          const int e = 2 * t + u, i = cc * 8 + e;
+          const float lse = e < 4 ? l0[e] : l1[e - 4];
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], c, -lse * kLog2e));
           pr2[u] = pr;
-          ds2[u] = pr * (pacc[0][i] - dl[i]);
+          ds2[u] = pr * (pacc[0][i] - dl);
         }
         wp[t] = Op::pack2(pr2[0], pr2[1]);
         wd[t] = Op::pack2(ds2[0], ds2[1]);
@@ -461,8 +481,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        dvacc[db] = Op::mfma(read_tr<frag, D>(orows + cc * 16 * RB, ta, db), pf[cc], dvacc[db]);
-        dkacc[db] = Op::mfma(read_tr<frag, D>(qrows + cc * 16 * RB, ta, db), dsf[cc], dkacc[db]);
+        dvacc[db] = Op::mfma(read_tr<frag, D>(orows + cc * 16 * RB, ta, db + D0 / 32), pf[cc], dvacc[db]);
+        dkacc[db] = Op::mfma(read_tr<frag, D>(qrows + cc * 16 * RB, ta, db + D0 / 32), dsf[cc], dkacc[db]);
       }
   };
 
@@ -482,7 +502,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void_t*)sts, 4, (tile * BN + lane) * 4, 0, 0, 0);
     else if (wave == 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void_t*)(sts + BN), 4, (tile * BN + lane) * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void_t*)(sts + SD), 4, (tile * BN + lane) * 4, 0, 0, 0);
   };
   // Every wave runs every block of its workgroup's tiles: a block before a
   // wave's first key (causal) or a wave past N is wholly masked or never
@@ -505,8 +525,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (k_ok) {
-    store_rowT<T, D>(p.dk + row_off, dkacc, p.scale, g);
-    store_rowT<T, D>(p.dv + row_off, dvacc, 1.f, g);
+    store_rowT<T, DO>(p.dk + row_off + D0 * 2, dkacc, p.scale, g);
+    store_rowT<T, DO>(p.dv + row_off + D0 * 2, dvacc, 1.f, g);
   }
 }
 
@@ -630,10 +650,10 @@ void attn_bwd_dkdv8_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(qrows + ta.rows[ks]));
+      const frag a = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(qrows + ta.row(ks)));
       const frag b = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(skv + kvaddr[ks]));
       sacc = Op::mfma(a, b, sacc);                     // S = Q K^T   (lane = key)
-      const frag a2 = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(orows + ta.rows[ks]));
+      const frag a2 = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(orows + ta.row(ks)));
       const frag b2 = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(skv + KVB + kvaddr[ks]));
       pacc = Op::mfma(a2, b2, pacc);                   // dP = dO V^T
     }
@@ -766,6 +786,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.total = a.B * a.H * p.nblk;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
+  if constexpr (D == 256) {
+    // both halves of each gradient's columns, each launch recomputing S and
+    // dP over the full d (the dq launches write delta first, read by dK/dV)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL, 0>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL, 1>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL, 0>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL, 1>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -782,6 +811,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, bool* ok) {
   switch (a.d) {
     case 64: return a.causal ? launch_bwd<T, 64, true>(a, s) : launch_bwd<T, 64, false>(a, s);
     case 128: return a.causal ? launch_bwd<T, 128, true>(a, s) : launch_bwd<T, 128, false>(a, s);
+    case 256: return a.causal ? launch_bwd<T, 256, true>(a, s) : launch_bwd<T, 256, false>(a, s);
   }
   *ok = false;
   return hipSuccess;

@@ -341,7 +341,7 @@ int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  *
  *   dtype          ATTN_F16 or ATTN_BF16 (ATTN_F32: ATTN_ERR_UNSUPPORTED):
  *                  type of q, k, v, o, dout, dq, dk, dv.
- *   B, H, N, d     as in attn_fwd; d in {64, 128} (256: ATTN_ERR_UNSUPPORTED).
+ *   B, H, N, d     as in attn_fwd; d in {64, 128, 256}.
  *   q, k, v        device [B, H, N, d] forward inputs.
  *   qkv_strides    host array of 3 int64 element strides (b, h, n) shared by
  *                  q, k and v, as in attn_fwd; NULL = contiguous.
@@ -355,8 +355,10 @@ int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  *   dq, dk, dv     device [B, H, N, d] outputs, contiguous, same dtype.
  *   softmax_scale, causal, stream   as in attn_fwd.
  *
- * Two launches on `stream` in order (dQ and D first, then dK and dV); no
- * atomics, so the result is bitwise reproducible.  Accumulation is fp32;
+ * Two launches on `stream` in order (dQ and D first, then dK and dV; at
+ * d = 256 four: each gradient's columns 0..127 and 128..255 in launches of
+ * their own, which both recompute P and dP over the full d); no atomics, so
+ * the result is bitwise reproducible.  Accumulation is fp32;
  * P and dS are rounded to the input dtype as operands of the second
  * products, and each gradient is rounded to the dtype once at the end.
  * Outputs and the workspace must not overlap each other or the inputs.

@@ -239,7 +239,6 @@ def _bwd(lib, dtype=2, B=1, H=2, N=100, d=128, scale=0.125, causal=0, strides=No
     (dict(lse=BW["lse"] + 2), 1, "not 4-byte aligned"),
     (dict(N=0), 1, "sizes must be positive"),
     (dict(dtype=0), 2, "fp16 / bf16"),
-    (dict(d=256), 2, "fp16 / bf16"),
     (dict(d=96), 2, "head dimension"),
     (dict(dtype=7), 1, "unknown dtype"),
     (dict(scale=0.0), 1, "softmax_scale"),

@@ -1,4 +1,4 @@
-"""GPU parity of attn_bwd (fp16 / bf16, d = 64 and 128) against the fp64
+"""GPU parity of attn_bwd (fp16 / bf16, d = 64, 128 and 256) against the fp64
 oracle's backward (oracle.attention_backward: the chain rule with S and P
 materialised).
 
@@ -64,7 +64,8 @@ def _oracle_fwd_bwd(x64, s, causal):
 
 
 SHAPES = [(1, 2, 256, 64), (1, 2, 300, 128), (2, 1, 129, 64), (1, 1, 1, 128), (1, 1, 33, 64),
-          (1, 3, 700, 128), (1, 1, 64, 128), (1, 2, 513, 64)]
+          (1, 3, 700, 128), (1, 1, 64, 128), (1, 2, 513, 64),
+          (1, 2, 300, 256), (2, 1, 129, 256), (1, 1, 1, 256), (1, 1, 32, 256)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
@@ -89,9 +90,10 @@ def test_bwd_matches_oracle(shape, causal, dtype):
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_forward_then_backward(causal):
+@pytest.mark.parametrize("d", [128, 256])
+def test_forward_then_backward(causal, d):
     """The GPU forward's O and LSE feed the GPU backward (the training use)."""
-    B, H, N, d = 2, 4, 1000, 128
+    B, H, N = 2, 4, 1000
     print(f"attn_fwd -> attn_bwd bf16 B={B} H={H} N={N} d={d} causal={causal}", flush=True)
     inp, do, s, x64 = _case(B, H, N, d, torch.bfloat16, causal, seed=7)
     dq_r, dk_r, dv_r = oracle.attention_backward(*x64, s, causal)
@@ -120,7 +122,7 @@ def test_bwd_softmax_scale():
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_bwd_strided_qkv(causal, d):
     """q, k, v as views of one packed [B, N, 3, H, d] projection (strides
     (N*3*H*d, d, 3*H*d)), the layout attn_fwd also accepts; o, dout and the
@@ -140,9 +142,10 @@ def test_bwd_strided_qkv(causal, d):
     _check(dv, dv_r, "dV")
 
 
-def test_bwd_deterministic():
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_deterministic(d):
     """No atomics: two calls give bitwise identical gradients."""
-    B, H, N, d = 2, 4, 777, 128
+    B, H, N = 2, 4, 777
     inp, do, s, _ = _case(B, H, N, d, torch.bfloat16, True, seed=13)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     o, lse = attn_fwd(q, k, v, causal=True)
