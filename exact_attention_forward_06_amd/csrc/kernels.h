@@ -102,7 +102,7 @@ hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream, bool* su
 hipError_t launch_attn_fwd16_pp_split(const FwdArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_attn_fwd16_pair_split(const FwdArgs& a, hipStream_t stream, bool* supported);
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream, bool* supported);
-// backward: dq kernel (also writes delta) then dk/dv kernel (fp16 / bf16, d = 64 and 128)
+// backward: dq kernel (also writes delta) then dk/dv kernel (fp16 / bf16, d = 64, 128 and 256)
 hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream, bool* supported);
 // measurement aid: shader cycles and 100 MHz ticks over spin_ticks ticks
 hipError_t launch_clock_probe(unsigned long long* out, long long spin_ticks, hipStream_t stream);

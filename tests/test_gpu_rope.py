@@ -70,6 +70,32 @@ def test_rope_base_and_e5m2():
 
 
 @pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_head_groups(style, d):
+    """Enough blocks that one workgroup walks several heads with one angle
+    cache (B=1, H=7, N=28160: 220 blocks per head, 3 heads per workgroup,
+    the last group partial): every head's codes and scales equal, bit for
+    bit, those of the same head quantised alone (one head per workgroup),
+    and the partial group's head matches the oracle."""
+    B, H, N = 1, 7, 28160
+    print(f"rope head groups {style} d={d}", flush=True)
+    inp = make_inputs(B, H, N, d, "bf16", seed=41 + d)
+    signs = random_signs(d, seed=43)
+    x, sg = inp["q"].cuda(), signs.cuda()
+    codes, scales = rope_hadamard_rotate_quant(x, sg, style=style, pos_offset=77)
+    for h in range(H):
+        c1, s1 = rope_hadamard_rotate_quant(x[:, h:h + 1], sg, style=style, pos_offset=77)
+        assert torch.equal(c1, codes[:, h:h + 1]), f"head {h}: codes differ from the single-head call"
+        assert torch.equal(s1, scales[:, h:h + 1]), f"head {h}: scales differ from the single-head call"
+    torch.cuda.synchronize()
+    c_ref, s_ref, y_ref = oracle.rope_hadamard_rotate_quant(to_f64(inp["q"][:, H - 1:]), signs.numpy(), 128,
+                                                            pos_offset=77, style=style)
+    np.testing.assert_allclose(scales[:, H - 1:].cpu().double().numpy(), s_ref, rtol=2e-6 + 2.0 ** -21)
+    band = _band(y_ref, d, True) + ROPE_BAND
+    _codes_match(codes[:, H - 1:].cpu().numpy(), c_ref, y_ref, band, f"rope head groups {style} d={d}")
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_fp8_attention_with_rope(style, causal):
     """FP8 attention on RoPE'd, rotated, quantised Q and K against the
