@@ -26,7 +26,7 @@ def _case(B, H, N, d, causal, seed):
         assert torch.equal(g, r), f"{name} differs from attn_bwd"
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_noalloc_matches_attn_bwd_twice(gpu_lib, d):
     _case(2, 3, 1000, d, True, seed=61)        # first call on the device
     _case(1, 2, 333, d, False, seed=62)        # a smaller one after it
