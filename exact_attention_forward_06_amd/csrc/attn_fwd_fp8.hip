@@ -86,6 +86,16 @@ __device__ __forceinline__ float wave_max64(float v) {
   return v;
 }
 
+// Largest block scale of a head's nblk scales: each lane loads every 64th
+// one (one round of vector loads for up to 64 blocks) and the wave reduces
+// them -- a loop of scalar loads would wait out one load latency per block
+// before the workgroup starts.
+__device__ __forceinline__ float head_max_scale(const float* s, int nblk, int lane) {
+  float m = 0.f;
+  for (int i = lane; i < nblk; i += 64) m = fmaxf(m, s[i]);
+  return wave_max64(m);
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // S^T accumulator row r of a 32-key block -> key: lane group g = bit 2 of r
@@ -197,8 +207,7 @@ void attn_fwd_fp8_kernel(F8Params p) {
   const float sq_raw = p.qs[(int64_t)bh * p.nblk + mb];
   const float sq = sq_raw > 0.f ? sq_raw : 1.f;
 
-  float svmax = 0.f;
-  for (int i = 0; i < p.nblk; ++i) svmax = fmaxf(svmax, vsc[i]);
+  float svmax = head_max_scale(p.vs + (int64_t)bh * p.nblk, p.nblk, lane);
   if (!(svmax > 0.f)) svmax = 1.f;     // every V block is zero: O = 0
   const float inv_svmax = 1.f / svmax;
 
@@ -449,8 +458,7 @@ void attn_fwd_fp8_pp_kernel(F8Params p) {
   typedef __attribute__((address_space(4))) const float cfloat_t;
   cfloat_t* ksc = (cfloat_t*)(p.ks + (int64_t)bh * p.nblk);
   cfloat_t* vsc = (cfloat_t*)(p.vs + (int64_t)bh * p.nblk);
-  float svmax = 0.f;
-  for (int i = 0; i < p.nblk; ++i) svmax = fmaxf(svmax, vsc[i]);
+  float svmax = head_max_scale(p.vs + (int64_t)bh * p.nblk, p.nblk, lane);
   if (!(svmax > 0.f)) svmax = 1.f;     // every V block is zero: O = 0
   const float inv_svmax = 1.f / svmax;
 
