@@ -196,16 +196,21 @@ def test_d256_split_tile_row_max(causal):
     _full_compare(inp, causal, torch.bfloat16, f"split-tile row max causal={causal}")
 
 
-def test_strided_bnhd_layout():
-    B, N, H, d = 2, 300, 4, 128
-    g = torch.Generator().manual_seed(3)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_strided_bnhd_layout(d, causal):
+    """q, k, v as [B, H, N, d] views of [B, N, H, d] tensors (n stride H*d),
+    for every kernel (d = 256 is the wave-pair kernel)."""
+    B, N, H = 2, 300, 4
+    print(f"attn_fwd strided d={d} causal={causal}", flush=True)
+    g = torch.Generator().manual_seed(3 + d)
     base = [torch.randn(B, N, H, d, generator=g).to(torch.bfloat16) for _ in range(3)]
     dev = [t.cuda().permute(0, 2, 1, 3) for t in base]       # [B, H, N, d] views, n stride H*d
     assert dev[0].stride() == (N * H * d, d, H * d, 1)
-    o, lse = attn_fwd(*dev, causal=True)
+    o, lse = attn_fwd(*dev, causal=causal)
     torch.cuda.synchronize()
     ref = [to_f64(t.permute(0, 2, 1, 3)) for t in base]
-    o_ref, lse_ref = oracle.attention(*ref, 1 / math.sqrt(d), True)
+    o_ref, lse_ref = oracle.attention(*ref, 1 / math.sqrt(d), causal)
     _check(to_f64(o), lse.cpu().double().numpy(), o_ref, lse_ref, torch.bfloat16, "strided")
 
 

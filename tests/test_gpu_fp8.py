@@ -36,7 +36,8 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_06_amd import attn_fwd_fp8, attn_fwd_fp8_e2e, attn_fwd_fp8_qrot, hadamard_rotate_quant
+from exact_attention_forward_06_amd import (attn_fwd_fp8, attn_fwd_fp8_e2e, attn_fwd_fp8_qrot, hadamard_rotate_quant,
+                                            rope_hadamard_rotate_quant)
 from exact_attention_forward_06_amd.inputs import WORKLOADS, make_inputs, random_signs, to_f64, workload_inputs
 
 from oracle_pool import fp8_head_errors, map_heads, reduce_fp8
@@ -144,6 +145,38 @@ def test_fp8_per_tensor_attention_matches_simulation(d, causal):
                                                     inp["signs"].numpy(), 1 / math.sqrt(d), causal, block_rows=N,
                                                     quantize_p=True, p_block=p_block(d))
     _check_sim(o, lse, o_ref, lse_ref, f"per-tensor d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_strided_inputs(d):
+    """The FP8 entry points on [B, H, N, d] views of [B, N, H, d] tensors:
+    the pre-pass (plain and with RoPE) and the attention with Q rotated in
+    the kernel give bitwise the results of the same data laid out
+    contiguously (the contiguous paths are checked against the oracle in
+    the tests above)."""
+    B, N, H = 2, 256, 3
+    print(f"fp8 strided inputs d={d}", flush=True)
+    g = torch.Generator().manual_seed(70 + d)
+    base = [torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).cuda() for _ in range(3)]
+    view = [t.permute(0, 2, 1, 3) for t in base]
+    cont = [t.contiguous() for t in view]
+    assert not view[0].is_contiguous() and view[0].stride() == (N * H * d, d, H * d, 1)
+    sg = random_signs(d, seed=71).cuda()
+    for args in ((sg,), (None,)):
+        c1, s1 = hadamard_rotate_quant(view[0], *args)
+        c2, s2 = hadamard_rotate_quant(cont[0], *args)
+        assert torch.equal(c1, c2) and torch.equal(s1, s2), f"pre-pass, signs={args[0] is not None}"
+    for style in ("interleaved", "half"):
+        c1, s1 = rope_hadamard_rotate_quant(view[1], sg, style=style, pos_offset=5)
+        c2, s2 = rope_hadamard_rotate_quant(cont[1], sg, style=style, pos_offset=5)
+        assert torch.equal(c1, c2) and torch.equal(s1, s2), f"rope pre-pass {style}"
+    if d <= 128:
+        k8, ks = hadamard_rotate_quant(cont[1], sg)
+        v8, vs = hadamard_rotate_quant(cont[2], None, transpose_out=True)
+        o1, l1 = attn_fwd_fp8_qrot(view[0], sg, k8, ks, v8, vs, causal=True)
+        o2, l2 = attn_fwd_fp8_qrot(cont[0], sg, k8, ks, v8, vs, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), "attn_fwd_fp8_qrot"
 
 
 def test_hadamard_block_max_encodes_to_448():

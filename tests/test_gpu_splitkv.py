@@ -148,3 +148,19 @@ def test_two_tilings_agree(dtype, d, causal):
         assert over1 <= 1e-3, f"splits={splits}: {over1:.2e} of the elements differ by more than 1 ulp"
         assert (diff > 0).double().mean().item() < 0.1, "the two tilings differ on many elements"
         assert (l1.double() - l2.double()).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_splitkv_strided_inputs(d):
+    """attn_fwd_splitkv on [B, H, N, d] views of [B, N, H, d] tensors gives
+    bitwise the result of the same data laid out contiguously."""
+    B, N, H = 1, 700, 3
+    print(f"split-KV strided d={d}", flush=True)
+    g = torch.Generator().manual_seed(80 + d)
+    base = [torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).cuda() for _ in range(3)]
+    view = [t.permute(0, 2, 1, 3) for t in base]
+    cont = [t.contiguous() for t in view]
+    o1, l1, _, _ = attn_fwd_splitkv(*view, 3, causal=True)
+    o2, l2, _, _ = attn_fwd_splitkv(*cont, 3, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
