@@ -105,6 +105,25 @@ def test_large_workload_sampled(name):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("N,d,causal", [(1 << 20, 64, True), (1 << 19, 128, False), (1 << 18, 256, True)])
+def test_long_sequence_sampled(N, d, causal):
+    """One head far longer than the workloads (up to 2^20 rows): every
+    kernel's index and offset arithmetic at large N, on rows sampled across
+    the whole sequence (the first and last rows, tile edges, random rows)
+    against the oracle, which evaluates each sampled row in full."""
+    print(f"attn_fwd long sequence N={N} d={d} causal={causal}", flush=True)
+    inp = make_inputs(1, 1, N, d, "bf16", seed=N + d)
+    o, lse = _run(inp, causal)
+    o, lse = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(N)
+    rows = {0, 1, 63, 64, 127, 128, 255, 256, N // 2 - 1, N // 2, N - 257, N - 256, N - 2, N - 1}
+    rows = np.array(sorted(rows | set(int(r) for r in rng.choice(N, 40, replace=False))))
+    q, k, v = (to_f64(inp[n][0, 0]) for n in ("q", "k", "v"))
+    o_r, l_r = oracle.attention_rows(q, k, v, rows, 1 / math.sqrt(d), causal)
+    _check(to_f64(o[0, 0])[rows], lse[0, 0].double().numpy()[rows], o_r, l_r, torch.bfloat16, f"long N={N} d={d}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
 @pytest.mark.parametrize("name", ["bf16_causal_8k", "bf16_d64", "bf16_d256"])
 def test_large_workload_full(name, capsys):
     """Every head and every row of the large bf16 workloads (the bench's

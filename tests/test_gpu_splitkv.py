@@ -164,3 +164,19 @@ def test_splitkv_strided_inputs(d):
     o2, l2, _, _ = attn_fwd_splitkv(*cont, 3, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_splitkv_long_sequence():
+    """Split-KV over a 2^19-row head (4 key ranges of 2^17 keys): the merged
+    output on sampled rows against the oracle."""
+    N, d = 1 << 19, 128
+    print(f"split-KV long sequence N={N}", flush=True)
+    inp = make_inputs(1, 1, N, d, "bf16", seed=91)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o, lse, _, _ = attn_fwd_splitkv(q, k, v, 4, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.array(sorted({0, 1, N - 1, N // 4 - 1, N // 4, N // 2} | set(int(r) for r in rng.choice(N, 40, False))))
+    o_r, l_r = oracle.attention_rows(to_f64(inp["q"][0, 0]), to_f64(inp["k"][0, 0]), to_f64(inp["v"][0, 0]),
+                                     rows, 1 / math.sqrt(d), True)
+    _check(to_f64(o[0, 0].cpu())[rows], lse[0, 0].cpu().double().numpy()[rows], o_r, l_r, "split-KV long")
