@@ -184,6 +184,30 @@ def attention_backward_head(q, k, v, do, scale, causal=False):
     return dq, dk, dv
 
 
+def attention_backward_rows(q, k, v, do, rows, scale, causal=False):
+    """dQ of attention_backward_head for a subset of query rows of one head
+    (q, k, v, do: [N, d]; rows: int indices).  Row i of dQ depends only on
+    query row i, its upstream gradient row and all keys and values, so each
+    sampled row is the gradient's definition evaluated for that row alone:
+
+        s_i = q_i K^T * scale (masked -inf),   p_i = softmax(s_i)
+        dp_i = dO_i V^T,   D_i = p_i . dp_i,   dq_i = (p_i o (dp_i - D_i)) K * scale
+
+    Used where a whole head's N x N matrices would take too long.  Returns
+    fp64 dQ[rows]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    s = (q[rows] @ k.T) * float(scale)
+    if causal:
+        j = np.arange(k.shape[0])[None, :]
+        s = np.where(j > rows[:, None], -np.inf, s)
+    p, _, _ = row_softmax(s)
+    dp = do[rows] @ v.T
+    dsum = np.sum(p * dp, axis=1)
+    ds = p * (dp - dsum[:, None])
+    return ds @ k * float(scale)
+
+
 def attention_backward(q, k, v, do, scale, causal=False):
     """Batched [..., N, d] version of attention_backward_head (one head at a
     time).  Returns fp64 (dQ, dK, dV)."""

@@ -189,3 +189,32 @@ def test_bwd_full_size(workload):
     res_v = np.abs(g_dv.sum(axis=2) - to_f64(do).sum(axis=2)).max()
     assert res_k <= 0.05 * walk_k, (res_k, walk_k)
     assert res_v <= 0.05 * walk_v, (res_v, walk_v)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_long_sequence(d):
+    """One causal head far longer than the workloads (2^17 rows; 2^16 at
+    d = 256): the GPU forward feeds the backward; dQ on rows sampled across
+    the sequence against the oracle row by row (oracle.attention_backward_rows),
+    and dK, dV over the whole head through the two identities of the exact
+    gradient (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i)."""
+    N = 1 << 17 if d == 128 else 1 << 16
+    print(f"attn_bwd long sequence N={N} d={d}", flush=True)
+    inp, do, s, x64 = _case(1, 1, N, d, torch.bfloat16, True, seed=200 + d)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o, lse = attn_fwd(q, k, v, causal=True)
+    dq, dk, dv, _ = attn_bwd(q, k, v, o, lse, do.cuda(), causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(N)
+    rows = {0, 1, 127, 128, 255, 256, N // 2, N - 129, N - 128, N - 2, N - 1}
+    rows = np.array(sorted(rows | set(int(r) for r in rng.choice(N, 40, replace=False))))
+    dq_r = oracle.attention_backward_rows(*(x[0, 0] for x in x64), rows, s, True)
+    _check(to_f64(dq[0, 0])[rows], dq_r, "dQ rows")
+    g_dk, g_dv = to_f64(dk[0, 0]), to_f64(dv[0, 0])
+    assert np.all(np.isfinite(g_dk)) and np.all(np.isfinite(g_dv))
+    walk_k = math.sqrt(N) * np.sqrt(np.mean(g_dk ** 2))
+    walk_v = math.sqrt(N) * np.sqrt(np.mean(g_dv ** 2))
+    res_k = np.abs(g_dk.sum(axis=0)).max()
+    res_v = np.abs(g_dv.sum(axis=0) - to_f64(do[0, 0]).sum(axis=0)).max()
+    assert res_k <= 0.05 * walk_k, (res_k, walk_k)
+    assert res_v <= 0.05 * walk_v, (res_v, walk_v)

@@ -379,3 +379,26 @@ def test_backward_invariants(causal):
     np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
     if causal:   # query 0 sees only key 0: its dS row is P_00 (dP_00 - D_0) = 0
         np.testing.assert_allclose(dq[0], 0.0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_rows_match_finite_differences(causal):
+    """attention_backward_rows against central differences of L = sum(dO * O)
+    in random directions of one query row at a time (the first-order
+    identity, independent of the full-head backward), and equal to the
+    full-head backward's rows."""
+    n, d = 11, 6
+    q, k, v, do = (_rand((n, d), s) for s in (93, 94, 95, 96))
+    scale = 0.6
+    rows = [0, 3, 10]
+    dq_rows = oracle.attention_backward_rows(q, k, v, do, rows, scale, causal)
+    rng = np.random.default_rng(97)
+    eps = 1e-6
+    for r_i, r in enumerate(rows):
+        for _ in range(3):
+            e = np.zeros((n, d))
+            e[r] = rng.standard_normal(d)
+            fd = (_loss(q + eps * e, k, v, do, scale, causal) - _loss(q - eps * e, k, v, do, scale, causal)) / (2 * eps)
+            assert abs(fd - float(np.dot(dq_rows[r_i], e[r]))) <= 1e-7 * max(1.0, abs(fd)), (r, fd)
+    dq, _, _ = oracle.attention_backward_head(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(dq_rows, dq[rows], rtol=0, atol=1e-12)
