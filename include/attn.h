@@ -29,8 +29,11 @@
  *  - N_q = N_k = N >= 1; d in {64, 128, 256}.  causal = 1 means query i sees
  *    keys 0..i.
  *  - The caller allocates and owns every buffer.  The library keeps no
- *    pointer after a call returns, allocates no device memory and has no
- *    global state; calls are thread-safe.  Outputs must not overlap inputs.
+ *    pointer to them after a call returns and allocates no device memory.
+ *    Its only state is the per-thread message of attn_last_error() and the
+ *    per-device scratch array of attn_bwd_noalloc (see there); calls are
+ *    thread-safe except overlapping attn_bwd_noalloc calls on one device.
+ *    Outputs must not overlap inputs.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *    stream) and is asynchronous: completion is observed by the caller.
  *  - Arguments are validated before any HIP call, so a rejected call has no
