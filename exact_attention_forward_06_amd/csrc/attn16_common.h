@@ -40,6 +40,7 @@ struct Params {
   float* o_part;        // fp32 [nsplit, B, H, N, d], each range's normalised O
   float* lse_part;      // fp32 [nsplit, B, H, N], each range's LSE (-inf if empty)
   int nsplit, chunk, bh_count;
+  int nwg;              // workgroups launched (a persistent grid takes several items each)
 };
 
 template <typename T>

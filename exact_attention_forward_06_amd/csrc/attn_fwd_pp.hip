@@ -69,8 +69,15 @@
 //  * Workgroup ids are remapped so that the Q blocks of a head run on one
 //    XCD (the head's K/V is then re-read from that XCD's L2); under the
 //    causal mask the Q blocks with the most K/V tiles are issued first.
+//  * Causal at d = 128 the grid is persistent, one workgroup per CU, each
+//    walking its XCD's items in a snake order; this removes the gap between
+//    one workgroup's end and the next one's start on a CU and evens out the
+//    per-CU totals of heavy and light causal blocks.
 #include "attn16_common.h"
 #include "kernels.h"
+
+#include <algorithm>
+#include <climits>
 
 #include <math.h>
 
@@ -115,9 +122,25 @@ void attn_fwd_pp_kernel(Params p) {
   const int g = lane >> 5;
   const int N = p.N;
 
-  // work item -> (head, key range, Q block); the items of one head and range
-  // are consecutive, so they land on one XCD and share its L2
-  const int logical = xcd_logical_id(blockIdx.x, p.total);
+  // Workgroup w runs on XCD w % 8 and takes the items of that XCD's
+  // contiguous share of the item list (one head's items are consecutive, so
+  // they share the XCD's L2).  With one workgroup per item that is the plain
+  // XCD grouping.  The causal kernel runs as a persistent grid instead (one
+  // workgroup per CU, p.nwg of them): no workgroup launch between items,
+  // and the XCD's items are taken in a snake order over its workgroups, so
+  // that with the heaviest blocks first in each head a round of heavy items
+  // is followed by a round of light ones and the workgroups' totals match
+  // (at d = 128; the loop's registers cost the d = 64 kernel spills).
+  constexpr bool PERSIST = CAUSAL && !SPLIT && D == 128;   // at d = 64 the loop costs spills
+  const int xw = blockIdx.x & 7, lw = blockIdx.x >> 3;
+  const int n_x = (p.total >> 3) + (xw < (p.total & 7) ? 1 : 0);
+  const int l0_x = xw * (p.total >> 3) + min(xw, p.total & 7);
+  const int w_x = (p.nwg >> 3) + (xw < (p.nwg & 7) ? 1 : 0);
+  for (int round = 0; round < (PERSIST ? INT_MAX : 1); ++round) {
+  const int s_item = round * w_x + ((round & 1) ? w_x - 1 - lw : lw);
+  if (s_item >= n_x) break;
+  if (round > 0) phase_barrier();    // the previous item's LDS reads are done
+  const int logical = l0_x + s_item;
   int bh, mb, split = 0;
   if constexpr (SPLIT) {
     bh = logical / (p.nmb * p.nsplit);
@@ -419,7 +442,7 @@ void attn_fwd_pp_kernel(Params p) {
         }
       if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = m_run * kLn2 + logf(l_tot);
     }
-    return;
+    return;    // a split-KV grid is never persistent: one item per workgroup
   }
   if (q_row < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -434,6 +457,7 @@ void attn_fwd_pp_kernel(Params p) {
         *(u32x2_t*)(orow + d0 * 2) = w;
       }
     if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
+  }
   }
 }
 
@@ -459,7 +483,14 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   p.o_part = a.o_part;
   p.lse_part = a.lse_part;
   p.total = p.bh_count * p.nmb * p.nsplit;
-  hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, BN, CAUSAL, SPLIT>), dim3(p.total), dim3(512), 0, stream, p);
+  p.nwg = p.total;
+  if constexpr (CAUSAL && !SPLIT && D == 128) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      p.nwg = std::min(p.total, cus);     // one resident workgroup per CU
+  }
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, BN, CAUSAL, SPLIT>), dim3(p.nwg), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
