@@ -164,6 +164,15 @@ def test_multi_tile_ragged(causal, d):
     _full_compare(inp, causal, torch.bfloat16, f"N=1000 d={d} causal={causal}")
 
 
+def test_causal_grid_more_items_than_cus():
+    # causal d = 128 runs as a persistent grid, one workgroup per CU: 3 * 5
+    # heads of 18 blocks of 256 rows are 270 items, more than the 256 CUs and
+    # not a multiple of 8, so the XCDs' shares differ (34 or 33 items), the
+    # workgroups of an XCD take two rounds and the second round is partial
+    inp = make_inputs(3, 5, 4500, 128, "bf16", seed=11)
+    _full_compare(inp, True, torch.bfloat16, "B=3 H=5 N=4500 d=128 causal (270 items)")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_tile_sum_above_threshold(causal, d):
