@@ -39,11 +39,14 @@
 //  * dkdv kernel: the mirror image: S = Q K^T and dP = dO V^T with lane = one
 //    key; P and dS are the B operands of dV^T += dO^T P and dK^T += Q^T dS,
 //    with dO^T and Q^T read transposed from the streamed tiles.
-//  * d = 256: a wave cannot hold its 32 stationary rows of both operands
-//    (128 VGPRs) beside a full-width accumulator, so each gradient is built
-//    in two launches over its column halves (DH = 0, 1), each recomputing S
-//    and dP over the full d from 32-row streamed tiles; dK / dV use the
-//    4-wave dkdv kernel (K and V in VGPRs, dK and dV halves in AGPRs).
+//  * d = 256, one wave per SIMD: the dq kernel holds Q and dO (128 VGPRs)
+//    and all of dQ^T (128 registers, which the compiler places in the
+//    accumulation half of the register file), so dQ takes one launch.  dK
+//    and dV together would need 256 accumulator registers beside K and V, so
+//    they are built in two launches over their column halves (DH = 0, 1),
+//    each recomputing S and dP over the full d from 32-row streamed tiles,
+//    with the 4-wave dkdv kernel (K and V in VGPRs, dK and dV halves in
+//    AGPRs).
 //  * Causal: the dq kernel never loads K/V tiles past its block's last
 //    query; the dkdv kernel starts at the first Q tile that can see its
 //    block's keys.  Element masks run only on tiles that straddle the
@@ -180,10 +183,7 @@ __device__ __forceinline__ void store_rowT(char* dst, const f32x16_t (&acc)[D / 
 // ---------------------------------------------------------------------------
 // dQ (and D_i).  Grid: (b, h, 128-query block), XCD-grouped per head; under
 // the causal mask the blocks with the most K/V tiles go first.
-// DH (d = 256 only): this launch accumulates dQ's columns 128 DH .. + 127;
-// S and dP always run over the full d, so the two halves' launches each
-// recompute them (a d = 256 wave cannot hold Q, dO and all of dQ at once).
-template <typename T, int D, bool CAUSAL, int DH = 0>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
 void attn_bwd_dq_kernel(BwdParams p) {
   using Op = Ops<T>;
@@ -191,9 +191,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NT = kBwdThreads, BN = D <= 128 ? kBwdTile : 32;
   constexpr int RB = D * 2;
   constexpr int TILE = BN * RB;
-  constexpr int DO = D <= 128 ? D : 128;      // dQ columns of this launch
-  constexpr int D0 = DH * DO;                 // ... starting here
-  constexpr int NKS = D / 16, NKB = BN / 32, NDB = DO / 32, NCC = BN / 16;
+  constexpr int NKS = D / 16, NKB = BN / 32, NDB = D / 32, NCC = BN / 16;
   constexpr int LOADS = TILE / (NT * 16);
   static_assert(TILE % (NT * 16) == 0, "tile split");
 
@@ -240,7 +238,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < 8; ++e) part = fmaf((float)of[e], (float)dof[ks][e], part);
     }
     delta = pair_sum(part);
-    if (q_ok && g == 0 && DH == 0) p.delta[head + q_row] = delta;
+    if (q_ok && g == 0) p.delta[head + q_row] = delta;
   }
   const float lse2 = q_ok ? p.lse[head + q_row] * kLog2e : 0.f;
 
@@ -300,7 +298,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc)
-        dqacc[db] = Op::mfma(read_tr<frag, D>(kt + cc * 16 * RB, ta, db + D0 / 32), dsf[cc], dqacc[db]);
+        dqacc[db] = Op::mfma(read_tr<frag, D>(kt + cc * 16 * RB, ta, db), dsf[cc], dqacc[db]);
   };
 
   // The tile offset goes into the per-lane offset, which the buffer range
@@ -345,7 +343,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
     if (j + 1 < n_tiles) step(j + 1, 1);
   }
 
-  if (q_ok) store_rowT<T, DO>(p.dq + row_off + D0 * 2, dqacc, p.scale, g);
+  if (q_ok) store_rowT<T, D>(p.dq + row_off, dqacc, p.scale, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -787,10 +785,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   if constexpr (D == 256) {
-    // both halves of each gradient's columns, each launch recomputing S and
-    // dP over the full d (the dq launches write delta first, read by dK/dV)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL, 0>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL, 1>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
+    // dQ in one launch (which writes delta, read by dK / dV), then both
+    // halves of dK's and dV's columns, each launch recomputing S and dP over
+    // the full d
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL, 0>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL, 1>), dim3(p.total), dim3(kBwdThreads), 0, stream, p);
     return hipGetLastError();

@@ -359,9 +359,9 @@ int rope_hadamard_rotate_quant(int in_dtype, int B, int H, int N, int d,
  *   softmax_scale, causal, stream   as in attn_fwd.
  *
  * Two launches on `stream` in order (dQ and D first, then dK and dV; at
- * d = 256 four: each gradient's columns 0..127 and 128..255 in launches of
- * their own, which both recompute P and dP over the full d); no atomics, so
- * the result is bitwise reproducible.  Accumulation is fp32;
+ * d = 256 three: dQ in one, then dK's and dV's columns 0..127 and 128..255
+ * in launches of their own, which both recompute P and dP over the full d);
+ * no atomics, so the result is bitwise reproducible.  Accumulation is fp32;
  * P and dS are rounded to the input dtype as operands of the second
  * products, and each gradient is rounded to the dtype once at the end.
  * Outputs and the workspace must not overlap each other or the inputs.
