@@ -156,21 +156,25 @@ def test_small_shapes(dtype, d, causal, N):
     _full_compare(inp, causal, dtype, f"{dtype} d={d} N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_multi_tile_ragged(causal, d):
+def test_multi_tile_ragged(causal, d, dtype):
     # several Q blocks and K/V tiles, ragged tail, B*H > 1
-    inp = make_inputs(2, 3, 1000, d, "bf16", seed=7 if d == 128 else 8)
-    _full_compare(inp, causal, torch.bfloat16, f"N=1000 d={d} causal={causal}")
+    sd = "bf16" if dtype == torch.bfloat16 else "fp16"
+    inp = make_inputs(2, 3, 1000, d, sd, seed=7 if d == 128 else 8)
+    _full_compare(inp, causal, dtype, f"N=1000 d={d} causal={causal} {sd}")
 
 
-def test_causal_grid_more_items_than_cus():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+def test_causal_grid_more_items_than_cus(dtype):
     # causal d = 128 runs as a persistent grid, one workgroup per CU: 3 * 5
     # heads of 18 blocks of 256 rows are 270 items, more than the 256 CUs and
     # not a multiple of 8, so the XCDs' shares differ (34 or 33 items), the
     # workgroups of an XCD take two rounds and the second round is partial
-    inp = make_inputs(3, 5, 4500, 128, "bf16", seed=11)
-    _full_compare(inp, True, torch.bfloat16, "B=3 H=5 N=4500 d=128 causal (270 items)")
+    sd = "bf16" if dtype == torch.bfloat16 else "fp16"
+    inp = make_inputs(3, 5, 4500, 128, sd, seed=11)
+    _full_compare(inp, True, dtype, f"B=3 H=5 N=4500 d=128 causal (270 items) {sd}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
