@@ -488,7 +488,9 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      p.nwg = std::min(p.total, cus);     // one resident workgroup per CU
+      // one resident workgroup per CU, and at least one per XCD share of
+      // the items (workgroup w takes share w % 8)
+      p.nwg = std::min(p.total, std::max(cus, 8));
   }
   hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, BN, CAUSAL, SPLIT>), dim3(p.nwg), dim3(512), 0, stream, p);
   return hipGetLastError();
