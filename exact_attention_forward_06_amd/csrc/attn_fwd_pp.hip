@@ -130,334 +130,334 @@ void attn_fwd_pp_kernel(Params p) {
   // and the XCD's items are taken in a snake order over its workgroups, so
   // that with the heaviest blocks first in each head a round of heavy items
   // is followed by a round of light ones and the workgroups' totals match
-  // (at d = 128; the loop's registers cost the d = 64 kernel spills).
-  constexpr bool PERSIST = CAUSAL && !SPLIT && D == 128;   // at d = 64 the loop costs spills
+  // (at d = 128; at d = 64 the loop's registers made the kernel spill).
+  constexpr bool PERSIST = CAUSAL && !SPLIT && D == 128;
   const int xw = blockIdx.x & 7, lw = blockIdx.x >> 3;
   const int n_x = (p.total >> 3) + (xw < (p.total & 7) ? 1 : 0);
   const int l0_x = xw * (p.total >> 3) + min(xw, p.total & 7);
   const int w_x = (p.nwg >> 3) + (xw < (p.nwg & 7) ? 1 : 0);
   for (int round = 0; round < (PERSIST ? INT_MAX : 1); ++round) {
-  const int s_item = round * w_x + ((round & 1) ? w_x - 1 - lw : lw);
-  if (s_item >= n_x) break;
-  if (round > 0) phase_barrier();    // the previous item's LDS reads are done
-  const int logical = l0_x + s_item;
-  int bh, mb, split = 0;
-  if constexpr (SPLIT) {
-    bh = logical / (p.nmb * p.nsplit);
-    const int rem = logical - bh * p.nmb * p.nsplit;
-    split = rem / p.nmb;
-    mb = rem - split * p.nmb;
-  } else {
-    bh = logical / p.nmb;
-    mb = logical - bh * p.nmb;
-  }
-  if (CAUSAL) mb = p.nmb - 1 - mb;
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  const int m0 = mb * BLOCK_M;
-  const int wq0 = m0 + wave * 32;
-  const int q_row = wq0 + n;
-  const int64_t head_off = ((int64_t)b * p.sb + (int64_t)h * p.sh) * 2;
-  const int rbg = (int)(p.sn * 2);         // global row pitch in bytes
-
-  // Q^T fragments (B operand): lane (n, g) holds Q[q][16 ks + 8 g .. + 8]
-  frag qf[NKS];
-  {
-    const char* src = p.q + head_off + (int64_t)q_row * rbg + g * 16;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (q_row < N) raw = *(const u32x4_t*)(src + ks * 32);
-      qf[ks] = __builtin_bit_cast(frag, raw);
+    const int s_item = round * w_x + ((round & 1) ? w_x - 1 - lw : lw);
+    if (s_item >= n_x) break;
+    if (round > 0) phase_barrier();    // the previous item's LDS reads are done
+    const int logical = l0_x + s_item;
+    int bh, mb, split = 0;
+    if constexpr (SPLIT) {
+      bh = logical / (p.nmb * p.nsplit);
+      const int rem = logical - bh * p.nmb * p.nsplit;
+      split = rem / p.nmb;
+      mb = rem - split * p.nmb;
+    } else {
+      bh = logical / p.nmb;
+      mb = logical - bh * p.nmb;
     }
-  }
+    if (CAUSAL) mb = p.nmb - 1 - mb;
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    const int m0 = mb * BLOCK_M;
+    const int wq0 = m0 + wave * 32;
+    const int q_row = wq0 + n;
+    const int64_t head_off = ((int64_t)b * p.sb + (int64_t)h * p.sh) * 2;
+    const int rbg = (int)(p.sn * 2);         // global row pitch in bytes
 
-  // K/V global -> LDS: lane l of wave w, DMA instruction t, writes LDS bytes
-  // (t*NT + w*64 + l) * 16 of the stage = row P / RB, physical chunk
-  // (P % RB) / 16, which holds logical chunk physical ^ swz(row).
-  const int64_t extent = ((int64_t)(N - 1) * p.sn + D) * 2;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), (short)0, (int)extent, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), (short)0, (int)extent, 0x00020000);
-  int dma_off[LOADS];
+    // Q^T fragments (B operand): lane (n, g) holds Q[q][16 ks + 8 g .. + 8]
+    frag qf[NKS];
+    {
+      const char* src = p.q + head_off + (int64_t)q_row * rbg + g * 16;
 #pragma unroll
-  for (int t = 0; t < LOADS; ++t) {
-    const int pos = (t * NTC + (tid & (NTC - 1))) * 16;
-    const int row = pos / RB;
-    const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
-    dma_off[t] = row * rbg + chunk * 16;
-  }
-
-  // LDS read addresses: K A-operand row kb*32 +
-  // key_of_row(n), logical chunk 2 ks + g; V^T A-operand via tr16 reads.
-  const int krow = key_of_row(n);
-  const int kswz = swz<D>(krow);
-  const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
-  const int vg = hq >> 1;
-  const int vcol0 = (hq & 1) * 16 + 4 * ta;
-  int kaddr[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) kaddr[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
-  int vaddr[NDB][2];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = vg * 8 + half * 4 + te;
-      const int col = db * 32 + vcol0;
-      vaddr[db][half] = row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4_t raw = {0u, 0u, 0u, 0u};
+        if (q_row < N) raw = *(const u32x4_t*)(src + ks * 32);
+        qf[ks] = __builtin_bit_cast(frag, raw);
+      }
     }
 
-  f32x16_t oacc[NDB];
+    // K/V global -> LDS: lane l of wave w, DMA instruction t, writes LDS bytes
+    // (t*NT + w*64 + l) * 16 of the stage = row P / RB, physical chunk
+    // (P % RB) / 16, which holds logical chunk physical ^ swz(row).
+    const int64_t extent = ((int64_t)(N - 1) * p.sn + D) * 2;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), (short)0, (int)extent, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), (short)0, (int)extent, 0x00020000);
+    int dma_off[LOADS];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;   // whole-number running max of scale * log2(e) * s (possibly stale by < kTau)
-  float l_run = 0.f;         // this lane's half of the running row sum
+    for (int t = 0; t < LOADS; ++t) {
+      const int pos = (t * NTC + (tid & (NTC - 1))) * 16;
+      const int row = pos / RB;
+      const int chunk = ((pos % RB) / 16) ^ swz<D>(row);
+      dma_off[t] = row * rbg + chunk * 16;
+    }
 
-  // keys [k_lo, kv_end) of this item, in tiles j_base .. j_base + n_tiles - 1
-  const int k_lo = SPLIT ? split * p.chunk : 0;
-  int kv_end = SPLIT ? min(N, k_lo + p.chunk) : N;
-  if (CAUSAL) kv_end = min(kv_end, m0 + BLOCK_M);
-  const int j_base = k_lo / BN;            // chunk is a multiple of 128, and BN divides 128
-  const int n_tiles = kv_end > k_lo ? (kv_end - k_lo + BN - 1) / BN : 0;
-  // tiles this wave needs (causal: keys up to its last row)
-  const int w_tiles =
-      (wq0 >= N) ? 0 : (CAUSAL ? max(0, min(n_tiles, (wq0 + 31) / BN + 1 - j_base)) : n_tiles);
-  if constexpr (SPLIT) {
-    if (n_tiles == 0) {   // the whole range is masked for this Q block: O = 0, LSE = -inf
+    // LDS read addresses: K A-operand row kb*32 +
+    // key_of_row(n), logical chunk 2 ks + g; V^T A-operand via tr16 reads.
+    const int krow = key_of_row(n);
+    const int kswz = swz<D>(krow);
+    const int hq = lane >> 4, jj = lane & 15, ta = jj & 3, te = jj >> 2;
+    const int vg = hq >> 1;
+    const int vcol0 = (hq & 1) * 16 + 4 * ta;
+    int kaddr[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kaddr[ks] = krow * RB + (((2 * ks + g) ^ kswz) * 16);
+    int vaddr[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row = vg * 8 + half * 4 + te;
+        const int col = db * 32 + vcol0;
+        vaddr[db][half] = row * RB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+      }
+
+    f32x16_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY;   // whole-number running max of scale * log2(e) * s (possibly stale by < kTau)
+    float l_run = 0.f;         // this lane's half of the running row sum
+
+    // keys [k_lo, kv_end) of this item, in tiles j_base .. j_base + n_tiles - 1
+    const int k_lo = SPLIT ? split * p.chunk : 0;
+    int kv_end = SPLIT ? min(N, k_lo + p.chunk) : N;
+    if (CAUSAL) kv_end = min(kv_end, m0 + BLOCK_M);
+    const int j_base = k_lo / BN;            // chunk is a multiple of 128, and BN divides 128
+    const int n_tiles = kv_end > k_lo ? (kv_end - k_lo + BN - 1) / BN : 0;
+    // tiles this wave needs (causal: keys up to its last row)
+    const int w_tiles =
+        (wq0 >= N) ? 0 : (CAUSAL ? max(0, min(n_tiles, (wq0 + 31) / BN + 1 - j_base)) : n_tiles);
+    if constexpr (SPLIT) {
+      if (n_tiles == 0) {   // the whole range is masked for this Q block: O = 0, LSE = -inf
+        if (q_row < N) {
+          float* orow = p.o_part + (((int64_t)split * p.bh_count + bh) * N + q_row) * D;
+#pragma unroll
+          for (int c = 0; c < D / 8; ++c) *(f32x4_t*)(orow + c * 8 + g * 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = -INFINITY;
+        }
+        return;
+      }
+    }
+    const float c = p.scale_log2;
+
+    f32x16_t sacc[NKB];
+    frag pf[NCC];
+
+    auto mask_tile = [&](int kt0) __attribute__((always_inline)) {   // kt0: global key index
+      const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt0 + kb * 32 + key_of_reg(i, g);
+            if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
+          }
+      }
+    };
+    auto tile_max = [&]() __attribute__((always_inline)) -> float {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      return pair_max(mx) * c;
+    };
+    auto update_max = [&](float m_tile) __attribute__((always_inline)) {
+      if (__any(m_tile > m_run + kTau)) {
+        // whole numbers: the rescale is an exact power of two, and P is rounded
+        // to 16 bits on a grid that does not depend on where the running max
+        // happened to lie (so other tilings of the keys round P identically)
+        const float m_new = ceilf(fmaxf(m_run, m_tile));
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_run = m_new;
+      }
+    };
+    // P_j = exp2(S_j c - m_run) into pf; returns this lane's sum of P
+    auto softmax_p = [&]() __attribute__((always_inline)) -> float {
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        const int kb = cc >> 1, base = (cc & 1) * 8;
+        u32x4_t w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t], c, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t + 1], c, -m_use));
+          w[t] = Op::pack2(e0, e1);
+          rs0 += e0;
+          rs1 += e1;
+        }
+        pf[cc] = __builtin_bit_cast(frag, w);
+      }
+      return rs0 + rs1;
+    };
+    // Softmax phase of the tile at global key kt0.  P is first taken against
+    // the running max as it stands.  A lane's sum of P bounds each of its P,
+    // so while no lane's sum exceeds 2^kTau no score of the tile is more than
+    // kTau above the running max and the lazy rescale would leave it where it
+    // is: the tile's max is then never needed.  Otherwise (and on a wave's
+    // first tile, where the running max is still -inf) the exact step runs:
+    // tile max, rescale rule, P again.  The running max thus follows the same
+    // sequence as with the max taken on every tile.  (One call site each for
+    // update_max and for the second softmax_p: the compiler copies all of O
+    // where control flow merges differently rescaled versions of it.)
+    auto softmax_tile = [&](int kt0) __attribute__((always_inline)) {
+      mask_tile(kt0);
+      float rs = 0.f;
+      bool exact = __any(m_run == -INFINITY);
+      if (!exact) {
+        rs = softmax_p();
+        exact = __any(rs > kRescaleSum);
+      }
+      if (exact) {
+        update_max(tile_max());
+        rs = softmax_p();
+      }
+      l_run += rs;
+    };
+
+    // MFMA phase: S^T of tile j from K stage `kst` (DQ) and O^T += V^T P^T of
+    // tile j-1 from V stage `vst` (DP).  MFMA pair i is S block i % NKB, K-step
+    // i / NKB and O block i % NDB, key chunk i / NDB; its operands are read
+    // from LDS LA pairs earlier.
+    auto phase_mfma = [&](auto dq_c, auto dp_c, const char* kst, const char* vst) __attribute__((always_inline)) {
+      constexpr bool DQ = decltype(dq_c)::value != 0, DP = decltype(dp_c)::value != 0;
+      frag kf[NOPS], vf[NOPS];
+      auto load = [&](int i) __attribute__((always_inline)) {
+        if constexpr (DQ)
+          kf[i] = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(kst + (i % NKB) * 32 * RB + kaddr[i / NKB]));
+        if constexpr (DP) {
+          const char* vb = vst + (i / NDB) * 16 * RB;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vaddr[i % NDB][0]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vaddr[i % NDB][1]));
+          u32x4_t w;
+          w[0] = __builtin_bit_cast(u32x2_t, lo)[0];
+          w[1] = __builtin_bit_cast(u32x2_t, lo)[1];
+          w[2] = __builtin_bit_cast(u32x2_t, hi)[0];
+          w[3] = __builtin_bit_cast(u32x2_t, hi)[1];
+          vf[i] = __builtin_bit_cast(frag, w);
+        }
+      };
+      __builtin_amdgcn_s_setprio(1);   // MFMA issue first when both waves of the SIMD are ready
+      if constexpr (DQ) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < LA && i < NOPS; ++i) load(i);
+#pragma unroll
+      for (int i = 0; i < NOPS; ++i) {
+        if (i + LA < NOPS) load(i + LA);
+        if constexpr (DQ) sacc[i % NKB] = Op::mfma(kf[i], qf[i / NKB], sacc[i % NKB]);
+        if constexpr (DP) oacc[i % NDB] = Op::mfma(vf[i], pf[i / NDB], oacc[i % NDB]);
+        // keep this order: the scheduler would otherwise pull each read down
+        // next to its MFMA and expose the LDS latency
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    // pair j = K_j (j < n_tiles) and V_{j-1} (j >= 1), into stage ST
+    auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
+      if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
+    };
+
+    // Phase t (t % 4 == TM) of group G.  Local phase u = t - G: even u = MFMA
+    // phase A_{u/2} (reads pair u/2), odd u = softmax phase B_{(u-1)/2}.  Pair
+    // j is read in phases 2j and 2j+1, copied during phase 2j-2 into stage
+    // j & 1 and waited for at the end of phase 2j-1.  The group is a template
+    // parameter so that each group's loop is straight-line code.
+    auto run = [&](auto g_c) __attribute__((always_inline)) {
+      constexpr int G = decltype(g_c)::value;
+      auto phase = [&](int t, auto tm_c) __attribute__((always_inline)) {
+        constexpr int TM = decltype(tm_c)::value;
+        if constexpr ((TM & 1) == 0 && G == 1) {
+          const int j = t / 2 + 1;
+          if (j <= n_tiles) copy_pair(j, ic<(TM == 0) ? 1 : 0>{});
+        }
+        const int u = t - G;
+        if (u >= 0 && u <= 2 * n_tiles) {
+          const int j = u >> 1;
+          if constexpr (((TM - G) & 1) == 0) {
+            constexpr int AST = TM >> 1;
+            const char* kst = AST ? sk1 : sk0;
+            const char* vst = AST ? sv1 : sv0;
+            // Both products run whenever either is needed: one code path keeps
+            // S and O in fixed registers (separate variants cost a copy of O
+            // per phase).  The unneeded one is harmless: S_j past the wave's
+            // last tile is never read, and in the first phase P is zero and V
+            // stage 0 is zero-filled, so O^T gains exactly zero.
+            if (j <= w_tiles) phase_mfma(ic<1>{}, ic<1>{}, kst, vst);
+          } else if (j < w_tiles) {
+            softmax_tile((j_base + j) * BN);
+          }
+        }
+        if constexpr ((TM & 1) == 1) wait_vmem();
+        if (t < 2 * n_tiles + 1) phase_barrier();
+      };
+      for (int t = 0; t < 2 * n_tiles + 2; t += 4) {
+        phase(t, ic<0>{});
+        phase(t + 1, ic<1>{});
+        if (t + 2 < 2 * n_tiles + 2) {
+          phase(t + 2, ic<2>{});
+          phase(t + 3, ic<3>{});
+        }
+      }
+    };
+
+    if (group == 1) copy_pair(0, ic<0>{});
+#pragma unroll
+    for (int c = 0; c < TILE / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) pf[cc] = frag{};
+    wait_vmem();
+    wait_lds();
+    phase_barrier();
+    if (group == 0) run(ic<0>{});
+    else run(ic<1>{});
+
+    // epilogue: O = O / l, LSE = m ln2 + ln l
+    const float l_tot = pair_sum(l_run);
+    if constexpr (SPLIT) {
       if (q_row < N) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float* orow = p.o_part + (((int64_t)split * p.bh_count + bh) * N + q_row) * D;
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) *(f32x4_t*)(orow + c * 8 + g * 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = -INFINITY;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int d0 = db * 32 + t * 8 + g * 4;
+            *(f32x4_t*)(orow + d0) = f32x4_t{oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv,
+                                              oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv};
+          }
+        if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = m_run * kLn2 + logf(l_tot);
       }
-      return;
+      return;    // a split-KV grid is never persistent: one item per workgroup
     }
-  }
-  const float c = p.scale_log2;
-
-  f32x16_t sacc[NKB];
-  frag pf[NCC];
-
-  auto mask_tile = [&](int kt0) __attribute__((always_inline)) {   // kt0: global key index
-    const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt0 + kb * 32 + key_of_reg(i, g);
-          if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
-        }
-    }
-  };
-  auto tile_max = [&]() __attribute__((always_inline)) -> float {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    return pair_max(mx) * c;
-  };
-  auto update_max = [&](float m_tile) __attribute__((always_inline)) {
-    if (__any(m_tile > m_run + kTau)) {
-      // whole numbers: the rescale is an exact power of two, and P is rounded
-      // to 16 bits on a grid that does not depend on where the running max
-      // happened to lie (so other tilings of the keys round P identically)
-      const float m_new = ceilf(fmaxf(m_run, m_tile));
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m_run = m_new;
-    }
-  };
-  // P_j = exp2(S_j c - m_run) into pf; returns this lane's sum of P
-  auto softmax_p = [&]() __attribute__((always_inline)) -> float {
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      const int kb = cc >> 1, base = (cc & 1) * 8;
-      u32x4_t w;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t], c, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][base + 2 * t + 1], c, -m_use));
-        w[t] = Op::pack2(e0, e1);
-        rs0 += e0;
-        rs1 += e1;
-      }
-      pf[cc] = __builtin_bit_cast(frag, w);
-    }
-    return rs0 + rs1;
-  };
-  // Softmax phase of the tile at global key kt0.  P is first taken against
-  // the running max as it stands.  A lane's sum of P bounds each of its P,
-  // so while no lane's sum exceeds 2^kTau no score of the tile is more than
-  // kTau above the running max and the lazy rescale would leave it where it
-  // is: the tile's max is then never needed.  Otherwise (and on a wave's
-  // first tile, where the running max is still -inf) the exact step runs:
-  // tile max, rescale rule, P again.  The running max thus follows the same
-  // sequence as with the max taken on every tile.  (One call site each for
-  // update_max and for the second softmax_p: the compiler copies all of O
-  // where control flow merges differently rescaled versions of it.)
-  auto softmax_tile = [&](int kt0) __attribute__((always_inline)) {
-    mask_tile(kt0);
-    float rs = 0.f;
-    bool exact = __any(m_run == -INFINITY);
-    if (!exact) {
-      rs = softmax_p();
-      exact = __any(rs > kRescaleSum);
-    }
-    if (exact) {
-      update_max(tile_max());
-      rs = softmax_p();
-    }
-    l_run += rs;
-  };
-
-  // MFMA phase: S^T of tile j from K stage `kst` (DQ) and O^T += V^T P^T of
-  // tile j-1 from V stage `vst` (DP).  MFMA pair i is S block i % NKB, K-step
-  // i / NKB and O block i % NDB, key chunk i / NDB; its operands are read
-  // from LDS LA pairs earlier.
-  auto phase_mfma = [&](auto dq_c, auto dp_c, const char* kst, const char* vst) __attribute__((always_inline)) {
-    constexpr bool DQ = decltype(dq_c)::value != 0, DP = decltype(dp_c)::value != 0;
-    frag kf[NOPS], vf[NOPS];
-    auto load = [&](int i) __attribute__((always_inline)) {
-      if constexpr (DQ)
-        kf[i] = __builtin_bit_cast(frag, *(const lds_u32x4_t*)(kst + (i % NKB) * 32 * RB + kaddr[i / NKB]));
-      if constexpr (DP) {
-        const char* vb = vst + (i / NDB) * 16 * RB;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vaddr[i % NDB][0]));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vaddr[i % NDB][1]));
-        u32x4_t w;
-        w[0] = __builtin_bit_cast(u32x2_t, lo)[0];
-        w[1] = __builtin_bit_cast(u32x2_t, lo)[1];
-        w[2] = __builtin_bit_cast(u32x2_t, hi)[0];
-        w[3] = __builtin_bit_cast(u32x2_t, hi)[1];
-        vf[i] = __builtin_bit_cast(frag, w);
-      }
-    };
-    __builtin_amdgcn_s_setprio(1);   // MFMA issue first when both waves of the SIMD are ready
-    if constexpr (DQ) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < LA && i < NOPS; ++i) load(i);
-#pragma unroll
-    for (int i = 0; i < NOPS; ++i) {
-      if (i + LA < NOPS) load(i + LA);
-      if constexpr (DQ) sacc[i % NKB] = Op::mfma(kf[i], qf[i / NKB], sacc[i % NKB]);
-      if constexpr (DP) oacc[i % NDB] = Op::mfma(vf[i], pf[i / NDB], oacc[i % NDB]);
-      // keep this order: the scheduler would otherwise pull each read down
-      // next to its MFMA and expose the LDS latency
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // pair j = K_j (j < n_tiles) and V_{j-1} (j >= 1), into stage ST
-  auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
-    if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
-  };
-
-  // Phase t (t % 4 == TM) of group G.  Local phase u = t - G: even u = MFMA
-  // phase A_{u/2} (reads pair u/2), odd u = softmax phase B_{(u-1)/2}.  Pair
-  // j is read in phases 2j and 2j+1, copied during phase 2j-2 into stage
-  // j & 1 and waited for at the end of phase 2j-1.  The group is a template
-  // parameter so that each group's loop is straight-line code.
-  auto run = [&](auto g_c) __attribute__((always_inline)) {
-    constexpr int G = decltype(g_c)::value;
-    auto phase = [&](int t, auto tm_c) __attribute__((always_inline)) {
-      constexpr int TM = decltype(tm_c)::value;
-      if constexpr ((TM & 1) == 0 && G == 1) {
-        const int j = t / 2 + 1;
-        if (j <= n_tiles) copy_pair(j, ic<(TM == 0) ? 1 : 0>{});
-      }
-      const int u = t - G;
-      if (u >= 0 && u <= 2 * n_tiles) {
-        const int j = u >> 1;
-        if constexpr (((TM - G) & 1) == 0) {
-          constexpr int AST = TM >> 1;
-          const char* kst = AST ? sk1 : sk0;
-          const char* vst = AST ? sv1 : sv0;
-          // Both products run whenever either is needed: one code path keeps
-          // S and O in fixed registers (separate variants cost a copy of O
-          // per phase).  The unneeded one is harmless: S_j past the wave's
-          // last tile is never read, and in the first phase P is zero and V
-          // stage 0 is zero-filled, so O^T gains exactly zero.
-          if (j <= w_tiles) phase_mfma(ic<1>{}, ic<1>{}, kst, vst);
-        } else if (j < w_tiles) {
-          softmax_tile((j_base + j) * BN);
-        }
-      }
-      if constexpr ((TM & 1) == 1) wait_vmem();
-      if (t < 2 * n_tiles + 1) phase_barrier();
-    };
-    for (int t = 0; t < 2 * n_tiles + 2; t += 4) {
-      phase(t, ic<0>{});
-      phase(t + 1, ic<1>{});
-      if (t + 2 < 2 * n_tiles + 2) {
-        phase(t + 2, ic<2>{});
-        phase(t + 3, ic<3>{});
-      }
-    }
-  };
-
-  if (group == 1) copy_pair(0, ic<0>{});
-#pragma unroll
-  for (int c = 0; c < TILE / (NT * 16); ++c) *(lds_u32x4_t*)(sv0 + (c * NT + tid) * 16) = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int cc = 0; cc < NCC; ++cc) pf[cc] = frag{};
-  wait_vmem();
-  wait_lds();
-  phase_barrier();
-  if (group == 0) run(ic<0>{});
-  else run(ic<1>{});
-
-  // epilogue: O = O / l, LSE = m ln2 + ln l
-  const float l_tot = pair_sum(l_run);
-  if constexpr (SPLIT) {
     if (q_row < N) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* orow = p.o_part + (((int64_t)split * p.bh_count + bh) * N + q_row) * D;
+      char* orow = p.o + (((int64_t)bh * N + q_row) * D) * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int d0 = db * 32 + t * 8 + g * 4;
-          *(f32x4_t*)(orow + d0) = f32x4_t{oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv,
-                                            oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv};
+          u32x2_t w = {Op::pack2(oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv),
+                       Op::pack2(oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv)};
+          *(u32x2_t*)(orow + d0 * 2) = w;
         }
-      if (g == 0) p.lse_part[((int64_t)split * p.bh_count + bh) * N + q_row] = m_run * kLn2 + logf(l_tot);
+      if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
     }
-    return;    // a split-KV grid is never persistent: one item per workgroup
-  }
-  if (q_row < N) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    char* orow = p.o + (((int64_t)bh * N + q_row) * D) * 2;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int d0 = db * 32 + t * 8 + g * 4;
-        u32x2_t w = {Op::pack2(oacc[db][4 * t] * inv, oacc[db][4 * t + 1] * inv),
-                     Op::pack2(oacc[db][4 * t + 2] * inv, oacc[db][4 * t + 3] * inv)};
-        *(u32x2_t*)(orow + d0 * 2) = w;
-      }
-    if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * N + q_row] = m_run * kLn2 + logf(l_tot);
-  }
   }
 }
 
