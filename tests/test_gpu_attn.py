@@ -256,9 +256,12 @@ def test_custom_scale_and_no_lse():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("d", [128, 256])
-def test_bitwise_deterministic(d):
-    inp = make_inputs(2, 4, 1500, d, "bf16", seed=11)
+@pytest.mark.parametrize("d,shape", [(128, (2, 4, 1500)), (256, (2, 4, 1500)),
+                                     (128, (2, 16, 4096))],   # 512 causal items: two rounds per CU
+                         ids=["d128", "d256", "d128-512items"])
+def test_bitwise_deterministic(d, shape):
+    B, H, N = shape
+    inp = make_inputs(B, H, N, d, "bf16", seed=11)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     o1, l1 = attn_fwd(q, k, v, causal=True)
     o2, l2 = attn_fwd(q, k, v, causal=True)
