@@ -93,7 +93,7 @@ __device__ __forceinline__ int swz(int row) {
 // land in with NaN first (and wait for those writes), so a read of a stage
 // before its copy has landed -- a missing wait or barrier -- turns into NaN
 // in the output instead of stale but plausible values.
-template <int LOADS, int NT>
+template <int LOADS, int NT, bool OPAQUE_WAVE = false>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int wave, int base, const int* off) {
 #ifdef ATTN_LDS_POISON
 #pragma unroll
@@ -102,9 +102,16 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, char* dst, i
         u32x4_t{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the NaN writes have landed
 #endif
+  // With OPAQUE_WAVE the wave's LDS offset is made opaque at each copy, so
+  // the M0 value of each instruction is one scalar add from it; otherwise the
+  // compiler keeps every (stage, t) address live across the tile loop, and in
+  // the forward kernels those SGPRs spill to VGPR lanes that each copy
+  // instruction reads back.
+  int wofs = wave * 64 * 16;
+  if constexpr (OPAQUE_WAVE) asm volatile("" : "+s"(wofs));
 #pragma unroll
   for (int t = 0; t < LOADS; ++t)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (t * NT + wave * 64) * 16), 16, off[t], base, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + t * NT * 16 + wofs), 16, off[t], base, 0, 0);
 }
 
 }  // namespace

@@ -313,8 +313,8 @@ void attn_fwd_pair_kernel(Params p) {
 
   auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
-    if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
-    if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
+    if (j < n_tiles) dma_tile<LOADS, NTC, true>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
+    if (j >= 1) dma_tile<LOADS, NTC, true>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
   };
 
   // The phase loop of attn_fwd_pp.hip: phase t (t % 4 == TM) of group G,

@@ -245,13 +245,16 @@ void attn_fwd_pp_kernel(Params p) {
     auto mask_tile = [&](int kt0) __attribute__((always_inline)) {   // kt0: global key index
       const bool need_mask = (kt0 + BN > N) || (CAUSAL && kt0 + BN - 1 > wq0);
       if (need_mask) {
+        // a key is masked where it lies past the last key the row may see
+        // (min(q_row, N - 1) under the causal mask, else N - 1); measured from
+        // the tile's first key and lane group g's offset, so that each
+        // register's test is one compare of a constant
+        const int lim = (CAUSAL ? min(q_row, N - 1) : N - 1) - kt0 - 8 * g;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt0 + kb * 32 + key_of_reg(i, g);
-            if ((key >= N) || (CAUSAL && key > q_row)) sacc[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + key_of_reg(i, 0) > lim) sacc[kb][i] = -INFINITY;
       }
     };
     auto tile_max = [&]() __attribute__((always_inline)) -> float {
@@ -368,8 +371,8 @@ void attn_fwd_pp_kernel(Params p) {
     // pair j = K_j (j < n_tiles) and V_{j-1} (j >= 1), into stage ST
     auto copy_pair = [&](int j, auto st_c) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
-      if (j < n_tiles) dma_tile<LOADS, NTC>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
-      if (j >= 1) dma_tile<LOADS, NTC>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
+      if (j < n_tiles) dma_tile<LOADS, NTC, true>(krs, ST ? sk1 : sk0, wave & 3, (j_base + j) * BN * rbg, dma_off);
+      if (j >= 1) dma_tile<LOADS, NTC, true>(vrs, ST ? sv1 : sv0, wave & 3, (j_base + j - 1) * BN * rbg, dma_off);
     };
 
     // Phase t (t % 4 == TM) of group G.  Local phase u = t - G: even u = MFMA
